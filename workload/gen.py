@@ -1,0 +1,317 @@
+"""Seeded generators of paged latent-KV decode inputs.
+
+Shapes and structure follow the workloads on the page "Kimi K3 decode: DP16 vs
+DP2 x DCP8": 96 query heads, 5 verified tokens per request, a 576-wide latent
+row per token (512 c_kv + 64 k_rope) stored once per token (VRAM page,
+"cell_size": pool shape (size + page_size, 1, 576)), an int32 request-to-slot
+table (VRAM page, "where the req_to_token size comes from"), FP8 storage at
+one byte per element (DP16-vs-DP2 page, "capacity": 24 layers x 576 B), and
+DCP shards holding positions p % 8 == r (same page, "problem" section).
+
+Every random draw is seeded from (config id, tensor id).  Index structure
+(lengths, page permutations, per-token scales) comes from numpy's
+SeedSequence-seeded generator and is identical on every machine; bulk values
+(queries and latent rows) come from a seeded torch generator on the target
+device, so large pools can be generated directly in GPU memory.
+
+Poisoning: page 0 is a padding page that no table entry references (the extra
+page_size slots of the pool), and slots past a request's length in its last
+page are filled with NaN (BF16 0x7FC0, e4m3fn 0x7F, scale NaN), so any read of
+a slot that should not be visible shows up as a NaN in the output.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+D_C = 512
+D_R = 64
+D_K = 576
+
+BF16_NAN_BITS = 0x7FC0
+E4M3FN_NAN_CODE = 0x7F
+
+# Tensor ids for the seed sequences.
+_T_LENGTHS, _T_PAGES, _T_SCALE, _T_KV, _T_QNOPE, _T_QROPE, _T_PLANT = range(7)
+
+
+def softmax_scale_default() -> float:
+    """fp32(1 / sqrt(192)); 192 = qk_nope_head_dim 128 + qk_rope_head_dim 64."""
+    return float(np.float32(1.0 / math.sqrt(192.0)))
+
+
+def kv_bytes_per_token(kv_dtype: str) -> int:
+    """Algorithmic KV bytes read per visible token: 576 elements (+ fp32 scale for FP8)."""
+    return D_K * 2 if kv_dtype == "bf16" else D_K * 1 + 4
+
+
+def _np_rng(cfg_id: int, tensor_id: int, extra: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([cfg_id, tensor_id, extra]))
+
+
+def _torch_gen(cfg_id: int, tensor_id: int, extra: int, device) -> torch.Generator:
+    seed = int(np.random.SeedSequence([cfg_id, tensor_id, extra]).generate_state(1, np.uint64)[0]
+               & ((1 << 63) - 1))
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def local_lengths(seq_lens, dcp_size: int, dcp_rank: int) -> np.ndarray:
+    """Number of positions p < L with p % W == r, for each global length L."""
+    L = np.asarray(seq_lens, dtype=np.int64)
+    n = (L - dcp_rank + dcp_size - 1) // dcp_size
+    return np.maximum(n, 0).astype(np.int64)
+
+
+def ragged_lengths(cfg_id: int, batch: int, lo: int, hi: int) -> np.ndarray:
+    """floor(exp(U(ln lo, ln hi))), seeded."""
+    u = _np_rng(cfg_id, _T_LENGTHS).uniform(math.log(lo), math.log(hi), size=batch)
+    return np.floor(np.exp(u)).astype(np.int64)
+
+
+@dataclass
+class DecodeInputs:
+    batch: int
+    q_len: int
+    num_heads: int
+    kv_dtype: str  # "bf16" | "fp8"
+    page_size: int
+    seq_lens: np.ndarray  # int64 [B], global lengths including the q drafts
+    local_lens: np.ndarray  # int64 [B], table columns used on this shard
+    q_nope: torch.Tensor  # bf16 [B, q, H, 512]
+    q_rope: torch.Tensor  # bf16 [B, q, H, 64]
+    pool: torch.Tensor  # bf16 [S, 576] or uint8 [S, 576]
+    kv_scale: torch.Tensor | None  # float32 [S] (FP8 only)
+    req_to_token: torch.Tensor  # int32 [B, stride]
+    softmax_scale: float
+    dcp_size: int = 1
+    dcp_rank: int = 0
+    name: str = ""
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_slots(self) -> int:
+        return int(self.pool.shape[0])
+
+    @property
+    def rows_per_request(self) -> int:
+        return self.q_len * self.num_heads
+
+    def kv_bytes(self) -> int:
+        """Algorithmic KV bytes: every stored token of every request read once."""
+        return int(self.local_lens.sum()) * kv_bytes_per_token(self.kv_dtype)
+
+    def to(self, device) -> "DecodeInputs":
+        d = dict(self.__dict__)
+        for k in ("q_nope", "q_rope", "pool", "kv_scale", "req_to_token"):
+            if d[k] is not None:
+                d[k] = d[k].to(device)
+        return DecodeInputs(**d)
+
+    def numpy_bits(self) -> dict:
+        """Stored bit patterns as numpy arrays, the form the oracle takes."""
+        return dict(
+            q_nope=self.q_nope.cpu().view(torch.int16).numpy().view(np.uint16),
+            q_rope=self.q_rope.cpu().view(torch.int16).numpy().view(np.uint16),
+            pool=(self.pool.cpu().view(torch.int16).numpy().view(np.uint16)
+                  if self.kv_dtype == "bf16" else self.pool.cpu().numpy()),
+            kv_scale=None if self.kv_scale is None else self.kv_scale.cpu().numpy(),
+            req_to_token=self.req_to_token.cpu().numpy(),
+            seq_lens=np.asarray(self.seq_lens, dtype=np.int64),
+        )
+
+
+def _page_table(cfg_id: int, local_lens: np.ndarray, page_size: int, extra: int):
+    """Request-to-slot table over a randomly permuted set of physical pages.
+
+    Page 0 is never referenced.  Returns (table int32 [B, stride], num_slots,
+    used bool [num_slots]).
+    """
+    B = len(local_lens)
+    pages = [int(math.ceil(n / page_size)) for n in local_lens]
+    total = sum(pages)
+    perm = _np_rng(cfg_id, _T_PAGES, extra).permutation(total) + 1
+    stride = max(page_size, int(math.ceil(max(local_lens, default=1) / page_size)) * page_size)
+    table = np.zeros((B, stride), dtype=np.int32)
+    used = np.zeros((total + 1) * page_size, dtype=bool)
+    k = 0
+    for b in range(B):
+        n = int(local_lens[b])
+        if n == 0:
+            continue
+        phys = perm[k:k + pages[b]]
+        k += pages[b]
+        j = np.arange(n)
+        slots = phys[j // page_size] * page_size + j % page_size
+        table[b, :n] = slots
+        used[slots] = True
+    return table, (total + 1) * page_size, used
+
+
+def _fill_values(shape, gen, device, dtype_out: str, std: float) -> torch.Tensor:
+    """N(0, 1) * std rounded to BF16 (RNE), or N(0, 1) rounded to e4m3fn bits."""
+    rows = shape[0]
+    out = torch.empty(shape, dtype=torch.bfloat16 if dtype_out == "bf16" else torch.uint8,
+                      device=device)
+    chunk = max(1, (1 << 26) // max(1, int(np.prod(shape[1:]))))
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        x = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=gen, device=device,
+                        dtype=torch.float32)
+        if dtype_out == "bf16":
+            out[r0:r1] = (x * std).to(torch.bfloat16)
+        else:
+            out[r0:r1] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    return out
+
+
+def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str,
+                page_size: int = 64, device="cpu", dcp_size: int = 1, dcp_rank: int = 0,
+                q_std: float = 0.1, kv_std: float = 0.1, scale_lo: float = 0.01,
+                scale_hi: float = 0.05, variant: str | None = None,
+                name: str = "") -> DecodeInputs:
+    """Build one decode call's inputs.
+
+    seq_lens are global lengths L_b (>= q_len).  With dcp_size > 1 the pool
+    and table hold only shard dcp_rank's positions p % W == r, at local index
+    (p - r) / W.  `variant` selects a peaked distribution for parity runs:
+    "qx30" (queries x 30), "planted" (1% of keys aligned with head 0's query),
+    "offset" (a large common score offset through the RoPE part).
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    B = len(seq_lens)
+    local = local_lengths(seq_lens, dcp_size, dcp_rank)
+    extra = dcp_rank if dcp_size > 1 else 0
+    table, num_slots, used = _page_table(cfg_id, local, page_size, extra)
+
+    kv_gen = _torch_gen(cfg_id, _T_KV, extra, device)
+    pool = _fill_values((num_slots, D_K), kv_gen, device, kv_dtype, kv_std)
+    kv_scale = None
+    if kv_dtype == "fp8":
+        sc = _np_rng(cfg_id, _T_SCALE, extra).uniform(scale_lo, scale_hi, size=num_slots)
+        kv_scale = torch.from_numpy(sc.astype(np.float32)).to(device)
+
+    q_mult = 30.0 if variant == "qx30" else 1.0
+    qn = _fill_values((B, q_len, num_heads, D_C), _torch_gen(cfg_id, _T_QNOPE, 0, device),
+                      device, "bf16", q_std * q_mult)
+    qr = _fill_values((B, q_len, num_heads, D_R), _torch_gen(cfg_id, _T_QROPE, 0, device),
+                      device, "bf16", q_std * q_mult)
+
+    if variant == "offset":
+        # A shared component along RoPE element 0 adds roughly the same large
+        # amount to every score, so exp() overflows unless the max is removed.
+        qr[..., 0] = 100.0
+        if kv_dtype == "bf16":
+            pool[:, D_C] = 40.0
+        else:
+            pool[:, D_C] = 0x7E  # e4m3fn 448
+    elif variant == "planted":
+        rng = _np_rng(cfg_id, _T_PLANT, extra)
+        q0 = torch.cat([qn[:, 0, 0].float(), qr[:, 0, 0].float()], dim=-1).cpu()  # [B, 576]
+        for b in range(B):
+            n = int(local[b])
+            k = max(1, n // 100)
+            js = rng.choice(n, size=k, replace=False)
+            slots = torch.from_numpy(table[b, js].astype(np.int64))
+            direction = q0[b] / q0[b].norm()
+            if kv_dtype == "bf16":
+                vals = (direction * 40.0).to(torch.bfloat16)
+                pool[slots.to(device)] = vals.to(device).expand(len(js), D_K)
+            else:
+                sc = kv_scale[slots.to(device)].cpu()
+                vals = (direction[None, :] * 40.0 / sc[:, None]).clamp(-448, 448)
+                pool[slots.to(device)] = vals.to(torch.float8_e4m3fn).view(torch.uint8).to(device)
+
+    unused = torch.from_numpy(~used).to(device)
+    if kv_dtype == "bf16":
+        pool.view(torch.int16)[unused] = BF16_NAN_BITS
+    else:
+        pool[unused] = E4M3FN_NAN_CODE
+        kv_scale[unused] = float("nan")
+
+    return DecodeInputs(
+        batch=B, q_len=q_len, num_heads=num_heads, kv_dtype=kv_dtype, page_size=page_size,
+        seq_lens=seq_lens, local_lens=local, q_nope=qn, q_rope=qr, pool=pool,
+        kv_scale=kv_scale, req_to_token=torch.from_numpy(table).to(device),
+        softmax_scale=softmax_scale_default(), dcp_size=dcp_size, dcp_rank=dcp_rank,
+        name=name, meta=dict(cfg_id=cfg_id, variant=variant))
+
+
+def shard_from_full(full: DecodeInputs, dcp_size: int, dcp_rank: int,
+                    cfg_id: int = 99) -> DecodeInputs:
+    """Shard dcp_rank of a full-context input: its own pool, pages and table.
+
+    Position p of request b (p % W == r) moves to local index (p - r) / W of a
+    freshly permuted shard pool; the latent rows and scales are copied
+    bit-for-bit, and the queries are shared (replicated on every shard).
+    """
+    W, r = dcp_size, dcp_rank
+    local = local_lengths(full.seq_lens, W, r)
+    table, num_slots, used = _page_table(cfg_id, local, full.page_size, 1000 + r)
+    dev = full.pool.device
+    pool = torch.empty((num_slots, D_K), dtype=full.pool.dtype, device=dev)
+    kv_scale = None if full.kv_scale is None else torch.full(
+        (num_slots,), float("nan"), dtype=torch.float32, device=dev)
+    full_table = full.req_to_token.cpu().numpy()
+    for b in range(full.batch):
+        n = int(local[b])
+        if n == 0:
+            continue
+        p = np.arange(n) * W + r
+        src = torch.from_numpy(full_table[b, p].astype(np.int64)).to(dev)
+        dst = torch.from_numpy(table[b, :n].astype(np.int64)).to(dev)
+        pool[dst] = full.pool[src]
+        if kv_scale is not None:
+            kv_scale[dst] = full.kv_scale[src]
+    unused = torch.from_numpy(~used).to(dev)
+    if full.kv_dtype == "bf16":
+        pool.view(torch.int16)[unused] = BF16_NAN_BITS
+    else:
+        pool[unused] = E4M3FN_NAN_CODE
+    return DecodeInputs(
+        batch=full.batch, q_len=full.q_len, num_heads=full.num_heads, kv_dtype=full.kv_dtype,
+        page_size=full.page_size, seq_lens=full.seq_lens.copy(), local_lens=local,
+        q_nope=full.q_nope, q_rope=full.q_rope, pool=pool, kv_scale=kv_scale,
+        req_to_token=torch.from_numpy(table).to(dev), softmax_scale=full.softmax_scale,
+        dcp_size=W, dcp_rank=r, name=f"{full.name}/shard{r}", meta=dict(full.meta, shard=r))
+
+
+# The five workloads.  Each is a decode call (or, for DCP, eight shard calls
+# and one merge) on one GPU.
+CONFIGS = {
+    1: dict(name="tiny-2x1.3k-q1-h16-bf16", seq_lens=[1024, 1536], q_len=1, num_heads=16,
+            kv_dtype="bf16"),
+    2: dict(name="standard-32x4096-q1-h128-bf16", seq_lens=[4096] * 32, q_len=1,
+            num_heads=128, kv_dtype="bf16"),
+    3: dict(name="mtp-16x100k-q5-h96-fp8", seq_lens=[100000] * 16, q_len=5, num_heads=96,
+            kv_dtype="fp8"),
+    4: dict(name="dcp8-128x100k-q5-h96-fp8", seq_lens=[100000] * 128, q_len=5, num_heads=96,
+            kv_dtype="fp8", dcp_size=8),
+    5: dict(name="sweep-200k-q5-h96-fp8", seq_len=200000, q_len=5, num_heads=96,
+            kv_dtype="fp8"),
+}
+SWEEP_BATCHES = (1, 2, 4, 8, 12, 16, 20, 24)
+
+
+def config_inputs(cfg_id: int, device="cpu", dcp_rank: int = 0, batch: int | None = None,
+                  ragged: bool = False) -> DecodeInputs:
+    """Inputs of workload `cfg_id` (for 4: shard `dcp_rank`; for 5: `batch` or ragged)."""
+    c = CONFIGS[cfg_id]
+    if cfg_id == 5:
+        if ragged:
+            lens = ragged_lengths(5, 64, 1024, 400000)
+            name = "sweep-ragged64-q5-h96-fp8"
+        else:
+            lens = [c["seq_len"]] * int(batch)
+            name = f"sweep-{batch}x200k-q5-h96-fp8"
+        return make_inputs(5, lens, c["q_len"], c["num_heads"], c["kv_dtype"], device=device,
+                           name=name)
+    kv_std = 0.1 if c["kv_dtype"] == "bf16" else 1.0
+    return make_inputs(cfg_id, c["seq_lens"], c["q_len"], c["num_heads"], c["kv_dtype"],
+                       device=device, dcp_size=c.get("dcp_size", 1), dcp_rank=dcp_rank,
+                       kv_std=kv_std, name=c["name"])
