@@ -1,0 +1,22 @@
+"""MI355X-native absorbed MLA decode attention over a paged latent KV cache.
+
+The compute runs in hand-written HIP kernels for gfx950 behind the C ABI of
+include/mla.h (libmla.so, built in this directory); this package only
+marshals arguments.  See `decode`, `make_plan`, `lse_combine`.
+"""
+
+from ._binding import (  # noqa: F401
+    KV_BF16,
+    KV_FP8,
+    DecodeDesc,
+    MlaError,
+    Plan,
+    decode,
+    library_path,
+    load_library,
+    lse_combine,
+    make_desc,
+    make_plan,
+    plan_max_bytes,
+    status_string,
+)

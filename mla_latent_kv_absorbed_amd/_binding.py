@@ -1,0 +1,239 @@
+"""ctypes binding of libmla (the C ABI declared in include/mla.h).
+
+Argument marshalling only: every step of the decode runs in the HIP kernels
+of libmla.  PyTorch provides device memory and the current HIP stream.  There
+is no fallback: if the library is not built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import struct
+from dataclasses import dataclass
+
+import numpy as np
+
+KV_BF16 = 0
+KV_FP8 = 1
+_KV_CODES = {"bf16": KV_BF16, "fp8": KV_FP8}
+
+MLA_OK = 0
+_STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape",
+           -3: "workspace or plan buffer too small", -4: "HIP runtime error"}
+
+
+class MlaError(RuntimeError):
+    def __init__(self, what: str, status: int | None = None):
+        super().__init__(what if status is None else f"{what}: {_STATUS.get(status, status)}")
+        self.status = status
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "q_len", "num_heads", "kv_lora_rank", "rope_dim", "page_size", "kv_dtype",
+        "dcp_size", "dcp_rank", "num_cus", "force_splits")]
+
+
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+
+
+def load_library():
+    """Load libmla.so from the package directory (raises if it is not built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise MlaError(f"{path} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    lib.mla_plan_max_bytes.argtypes = [ctypes.POINTER(DecodeDesc)]
+    lib.mla_plan_max_bytes.restype = sz
+    lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, sz,
+                                    ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.mla_decode_plan.restype = i32
+    lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, i64, vp, ctypes.c_float,
+                               vp, sz, vp, vp, vp]
+    lib.mla_decode.restype = i32
+    lib.mla_lse_combine.argtypes = [vp, vp, i32, i64, vp, vp, vp]
+    lib.mla_lse_combine.restype = i32
+    lib.mla_status_string.argtypes = [i32]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mla_status_string(status).decode()
+
+
+# Plan header fields, in the order of mla::PlanHeader (csrc/plan_layout.h).
+_HEADER = struct.Struct("<2I18i3q")
+_HEADER_NAMES = ("magic", "version", "batch", "q_len", "num_heads", "rows", "row_groups",
+                 "num_wgs", "num_units", "num_parts", "num_split_reqs", "kv_dtype", "dcp_size",
+                 "dcp_rank", "off_wg", "off_units", "off_reqs", "off_split", "max_local",
+                 "page_size", "plan_bytes", "workspace_bytes", "ws_lse_offset")
+
+
+def _aligned_bytes(n: int) -> np.ndarray:
+    raw = np.zeros(n + 64, dtype=np.uint8)
+    off = (-raw.ctypes.data) % 64
+    return raw[off:off + n]
+
+
+@dataclass
+class Plan:
+    """A decode plan: the host blob, its header fields and (optionally) a device copy."""
+    desc: DecodeDesc
+    host: np.ndarray  # uint8, exactly plan_bytes long, 64-byte aligned
+    header: dict
+    device: object = None  # torch uint8 tensor on the GPU
+
+    @property
+    def workspace_bytes(self) -> int:
+        return self.header["workspace_bytes"]
+
+    def wg_begin(self) -> np.ndarray:
+        h = self.header
+        return self.host[h["off_wg"]:h["off_wg"] + 4 * (h["num_wgs"] + 1)].view(np.int32)
+
+    def units(self) -> np.ndarray:
+        """int32 [num_units, 8]: b, g, j0, j1, part, pad, pad, pad."""
+        h = self.header
+        return self.host[h["off_units"]:h["off_units"] + 32 * h["num_units"]].view(
+            np.int32).reshape(-1, 8)
+
+    def req_parts(self) -> np.ndarray:
+        h = self.header
+        return self.host[h["off_reqs"]:h["off_reqs"] + 8 * h["batch"]].view(
+            np.int32).reshape(-1, 2)
+
+    def split_reqs(self) -> np.ndarray:
+        h = self.header
+        return self.host[h["off_split"]:h["off_split"] + 4 * h["num_split_reqs"]].view(np.int32)
+
+    def to_device(self, device="cuda"):
+        import torch
+        self.device = torch.from_numpy(self.host.copy()).to(device)
+        return self
+
+
+def make_desc(batch: int, q_len: int, num_heads: int, kv_dtype="bf16", page_size: int = 64,
+              dcp_size: int = 1, dcp_rank: int = 0, num_cus: int = 0,
+              force_splits: int = 0) -> DecodeDesc:
+    kv = _KV_CODES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
+    return DecodeDesc(batch, q_len, num_heads, 512, 64, page_size, kv, dcp_size, dcp_rank,
+                      num_cus, force_splits)
+
+
+def plan_max_bytes(desc: DecodeDesc) -> int:
+    return int(load_library().mla_plan_max_bytes(ctypes.byref(desc)))
+
+
+def make_plan(desc: DecodeDesc, seq_lens, device=None) -> Plan:
+    """Run the host planner (mla_decode_plan) for global lengths seq_lens."""
+    lib = load_library()
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    if lens.shape != (desc.batch,):
+        raise MlaError(f"seq_lens must have {desc.batch} entries")
+    cap = plan_max_bytes(desc)
+    if cap == 0:
+        raise MlaError("invalid decode description")
+    buf = _aligned_bytes(cap)
+    nbytes, ws = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = lib.mla_decode_plan(ctypes.byref(desc), lens.ctypes.data, buf.ctypes.data, cap,
+                             ctypes.byref(nbytes), ctypes.byref(ws))
+    if st != MLA_OK:
+        raise MlaError("mla_decode_plan failed", st)
+    host = buf[:nbytes.value]
+    header = dict(zip(_HEADER_NAMES, _HEADER.unpack_from(host.tobytes(), 0)))
+    p = Plan(desc=desc, host=host, header=header)
+    if device is not None:
+        p.to_device(device)
+    return p
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def decode(plan: Plan, q_nope, q_rope, kv_pool, kv_scale, req_to_token, seq_lens,
+           softmax_scale: float, workspace=None, out=None, lse=None, stream=None):
+    """mla_decode on torch device tensors; allocates out / lse / workspace if not given."""
+    import torch
+    h = plan.header
+    if plan.device is None:
+        raise MlaError("plan has no device copy (call plan.to_device())")
+    B, M = h["batch"], h["rows"]
+    dev = q_nope.device
+    for name, t in (("q_nope", q_nope), ("q_rope", q_rope), ("kv_pool", kv_pool),
+                    ("req_to_token", req_to_token), ("seq_lens", seq_lens)):
+        if t.device != dev or not t.is_contiguous():
+            raise MlaError(f"{name} must be a contiguous tensor on {dev}")
+    if q_nope.dtype != torch.bfloat16 or q_rope.dtype != torch.bfloat16:
+        raise MlaError("q_nope / q_rope must be bfloat16")
+    if tuple(q_nope.shape) != (B, h["q_len"], h["num_heads"], 512) or \
+            tuple(q_rope.shape) != (B, h["q_len"], h["num_heads"], 64):
+        raise MlaError("query shapes do not match the plan")
+    fp8 = h["kv_dtype"] == KV_FP8
+    want_pool = torch.uint8 if fp8 else torch.bfloat16
+    if kv_pool.dtype not in ((want_pool, torch.float8_e4m3fn) if fp8 else (want_pool,)) or \
+            kv_pool.dim() != 2 or kv_pool.shape[1] != 576:
+        raise MlaError("kv_pool must be [num_slots, 576] of the plan's dtype")
+    if fp8 and (kv_scale is None or kv_scale.dtype != torch.float32 or
+                kv_scale.numel() < kv_pool.shape[0] or kv_scale.device != dev):
+        raise MlaError("FP8 pools need an fp32 kv_scale per slot on the same device")
+    if req_to_token.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise MlaError("req_to_token and seq_lens must be int32")
+    if req_to_token.dim() != 2 or req_to_token.shape[0] != B:
+        raise MlaError("req_to_token must be [batch, stride]")
+    if out is None:
+        out = torch.empty((B, h["q_len"], h["num_heads"], 512), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, h["q_len"], h["num_heads"]), dtype=torch.float32, device=dev)
+    ws_bytes = h["workspace_bytes"]
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = load_library().mla_decode(
+        plan.host.ctypes.data, _ptr(plan.device), _ptr(q_nope), _ptr(q_rope), _ptr(kv_pool),
+        _ptr(kv_scale if fp8 else None), int(kv_pool.shape[0]), _ptr(req_to_token),
+        int(req_to_token.shape[1]), _ptr(seq_lens), float(softmax_scale), _ptr(workspace),
+        0 if workspace is None else int(workspace.numel() * workspace.element_size()),
+        _ptr(out), _ptr(lse), _stream(stream))
+    if st != MLA_OK:
+        raise MlaError("mla_decode failed", st)
+    return out, lse
+
+
+def lse_combine(part_o, part_lse, out=None, lse=None, stream=None):
+    """mla_lse_combine: merge [P, ..., 512] / [P, ...] partials into [..., 512] / [...]."""
+    import torch
+    P = part_o.shape[0]
+    rows = int(np.prod(part_o.shape[1:-1])) if part_o.dim() > 2 else part_o.shape[1]
+    if part_o.shape[-1] != 512 or tuple(part_lse.shape) != tuple(part_o.shape[:-1]):
+        raise MlaError("part_o must be [P, ..., 512] and part_lse [P, ...]")
+    if not (part_o.is_contiguous() and part_lse.is_contiguous()):
+        raise MlaError("partials must be contiguous")
+    if part_o.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise MlaError("partials must be float32")
+    if out is None:
+        out = torch.empty(part_o.shape[1:], dtype=torch.float32, device=part_o.device)
+    if lse is None:
+        lse = torch.empty(part_lse.shape[1:], dtype=torch.float32, device=part_o.device)
+    st = load_library().mla_lse_combine(_ptr(part_o), _ptr(part_lse), int(P), int(rows),
+                                        _ptr(out), _ptr(lse), _stream(stream))
+    if st != MLA_OK:
+        raise MlaError("mla_lse_combine failed", st)
+    return out, lse

@@ -1,0 +1,35 @@
+// Interface between the host code (mla_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Arguments of the decode kernel (device pointers unless noted).
+struct DecodeArgs {
+  const uint8_t* plan;       // device copy of the plan blob
+  const uint16_t* q_nope;    // bf16 bits [B, M, 512]
+  const uint16_t* q_rope;    // bf16 bits [B, M, 64]
+  const uint8_t* pool;       // [num_slots, 576] bf16 or e4m3fn elements
+  const float* kv_scale;     // [num_slots] (FP8)
+  int64_t num_slots;
+  const int32_t* table;      // [B, stride]
+  int64_t table_stride;
+  const int32_t* seq_lens;   // [B] global lengths
+  float c2;                  // softmax_scale * log2(e)
+  float* out;                // [B, M, 512]
+  float* lse;                // [B, M]
+  float* ws_o;               // [parts, M, 512]
+  float* ws_lse;             // [parts, M]
+};
+
+hipError_t launch_decode(bool fp8, bool paged, int grid, const DecodeArgs& args,
+                         hipStream_t stream);
+hipError_t launch_merge_split(const uint8_t* plan_dev, int num_split_reqs, int rows,
+                              const float* ws_o, const float* ws_lse, float* out, float* lse,
+                              hipStream_t stream);
+hipError_t launch_lse_combine(const float* part_o, const float* part_lse, int nparts,
+                              int64_t rows, float* out, float* lse, hipStream_t stream);
+
+}  // namespace mla

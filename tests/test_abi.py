@@ -1,0 +1,133 @@
+"""The C-ABI library: loads, exports every declared symbol, validates arguments.
+
+CPU only: nothing here launches a kernel (plans are made with an explicit
+compute-unit count, so no device is queried).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_latent_kv_absorbed_amd as mla
+from mla_latent_kv_absorbed_amd._binding import DecodeDesc, MlaError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(mla_\w+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mla.load_library()
+    names = declared_functions()
+    assert {"mla_decode_plan", "mla_decode", "mla_lse_combine"} <= names
+    for n in sorted(names):
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_status_strings():
+    for code, text in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported shape"),
+                       (-3, "workspace or plan buffer too small"), (-4, "HIP runtime error")]:
+        assert mla.status_string(code) == text
+
+
+def _desc(**kw):
+    base = dict(batch=2, q_len=5, num_heads=96, kv_dtype="fp8", page_size=64, num_cus=256)
+    base.update(kw)
+    return mla.make_desc(**base)
+
+
+@pytest.mark.parametrize("bad", [dict(batch=0), dict(q_len=0), dict(q_len=9), dict(num_heads=0),
+                                 dict(page_size=0), dict(dcp_size=0), dict(dcp_rank=8, dcp_size=8),
+                                 dict(dcp_rank=-1), dict(kv_dtype=7), dict(num_cus=-1),
+                                 dict(force_splits=-2)])
+def test_plan_rejects_invalid_descriptions(bad):
+    d = _desc(**bad)
+    assert mla.plan_max_bytes(d) == 0
+    with pytest.raises(MlaError):
+        mla.make_plan(d, [100] * max(1, d.batch))
+
+
+def test_plan_rejects_unsupported_dims():
+    d = DecodeDesc(1, 1, 16, 256, 64, 64, 0, 1, 0, 256, 0)
+    lib = mla.load_library()
+    buf = np.zeros(4096, np.uint8)
+    n, ws = ctypes.c_size_t(), ctypes.c_size_t()
+    lens = np.array([100], np.int32)
+    st = lib.mla_decode_plan(ctypes.byref(d), lens.ctypes.data, buf.ctypes.data, buf.size,
+                             ctypes.byref(n), ctypes.byref(ws))
+    assert st == -2
+
+
+def test_plan_rejects_short_lengths_and_small_buffers():
+    d = _desc()
+    with pytest.raises(MlaError, match="invalid"):
+        mla.make_plan(d, [4, 100])  # seq_len < q_len
+    lib = mla.load_library()
+    buf = np.zeros(64, np.uint8)
+    n, ws = ctypes.c_size_t(), ctypes.c_size_t()
+    lens = np.array([100, 100], np.int32)
+    st = lib.mla_decode_plan(ctypes.byref(d), lens.ctypes.data, buf.ctypes.data, 64,
+                             ctypes.byref(n), ctypes.byref(ws))
+    assert st == -3
+
+
+def test_decode_and_combine_reject_bad_arguments_on_host():
+    lib = mla.load_library()
+    p = mla.make_plan(_desc(), [100, 200])
+    # null pointers
+    st = lib.mla_decode(p.host.ctypes.data, None, None, None, None, None, 1, None, 1, None,
+                        ctypes.c_float(0.1), None, 0, None, None, None)
+    assert st == -1
+    # corrupted plan magic
+    bad = p.host.copy()
+    bad[:4] = 0
+    fake = 1 << 20  # never dereferenced: validation fails first
+    st = lib.mla_decode(bad.ctypes.data, fake, fake, fake, fake, fake, 10, fake, 1024, fake,
+                        ctypes.c_float(0.1), fake, 1 << 30, fake, fake, None)
+    assert st == -1
+    # misaligned pointer
+    st = lib.mla_decode(p.host.ctypes.data, fake + 4, fake, fake, fake, fake, 10, fake, 1024,
+                        fake, ctypes.c_float(0.1), fake, 1 << 30, fake, fake, None)
+    assert st == -1
+    # table stride smaller than the longest local length
+    st = lib.mla_decode(p.host.ctypes.data, fake, fake, fake, fake, fake, 10, fake, 100, fake,
+                        ctypes.c_float(0.1), fake, 1 << 30, fake, fake, None)
+    assert st == -1
+    # workspace too small (a plan that splits requests needs one)
+    ps = mla.make_plan(_desc(force_splits=2), [100, 200])
+    assert ps.workspace_bytes > 0
+    st = lib.mla_decode(ps.host.ctypes.data, fake, fake, fake, fake, fake, 10, fake, 1024, fake,
+                        ctypes.c_float(0.1), fake, ps.workspace_bytes - 256, fake, fake, None)
+    assert st == -3
+    # FP8 without scales
+    st = lib.mla_decode(p.host.ctypes.data, fake, fake, fake, fake, None, 10, fake, 1024, fake,
+                        ctypes.c_float(0.1), fake, 1 << 30, fake, fake, None)
+    assert st == -1
+    # non-finite scale
+    st = lib.mla_decode(p.host.ctypes.data, fake, fake, fake, fake, fake, 10, fake, 1024, fake,
+                        ctypes.c_float(float("nan")), fake, 1 << 30, fake, fake, None)
+    assert st == -1
+    assert lib.mla_lse_combine(None, None, 0, 10, None, None, None) == -1
+    assert lib.mla_lse_combine(fake, fake, 2, 0, fake, fake, None) == 0  # nothing to do
+    assert lib.mla_lse_combine(fake + 4, fake, 2, 5, fake, fake, None) == -1
+
+
+def test_plan_header_fields():
+    p = mla.make_plan(_desc(batch=3, dcp_size=8, dcp_rank=5), [100000, 8, 6])
+    h = p.header
+    assert h["magic"] == 0x504C414D and h["version"] == 1
+    assert h["rows"] == 480 and h["row_groups"] == 4
+    assert h["max_local"] == 12500 and h["dcp_size"] == 8 and h["dcp_rank"] == 5
+    assert h["plan_bytes"] == len(p.host) and h["page_size"] == 64
