@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of absorbed MLA decode on one MI355X.
+
+One step = one mla_decode call (one MLA layer for the whole batch, including
+the merge of split requests) on inputs already resident in HBM.  The default
+workload is the per-GPU share the pages time their B200 kernels on: 16
+requests x 100000 tokens, q_len 5 (causal among the drafts), 96 heads, FP8
+e4m3fn latent KV with a per-token scale, BF16 queries.
+
+Prints ONE JSON line (metric: us/layer, lower is better) with a `roofline`
+object for the decode kernel and a `cpu_baseline` object (the float64 oracle
+timed on a bounded sample of the same workload, scaled to the whole layer).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode us/layer + achieved KV HBM TB/s (% of peak) at 100k ctx, q_len 5"
+HBM_PEAK_TBPS = 8.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+B200_CONTEXT_US = {"mtp": 1240.0, "dcp8": 826.0}  # the pages' numbers (other hardware)
+
+WORKLOADS = {
+    "mtp": 3,       # 16 x 100k, q5, h96, fp8  (default)
+    "standard": 2,  # 32 x 4096, q1, h128, bf16
+    "tiny": 1,      # 2 x {1024, 1536}, q1, h16, bf16
+    "dcp8": 4,      # one shard of 128 x 100k over 8 shards, q5, h96, fp8
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_counts(x):
+    """FLOPs and bytes the method needs, independent of the implementation.
+
+    FLOPs: 2 x (576 + 512) per (query row, visible token); visible tokens of
+    draft row i are the positions p <= L - q + i held by this shard.
+    Bytes: every stored token's latent row (+ its fp32 scale for FP8) read
+    once, the queries read once, O and LSE written once.
+    """
+    from workload import kv_bytes_per_token
+    W, r, q, H = x.dcp_size, x.dcp_rank, x.q_len, x.num_heads
+    vis = 0
+    for L in x.seq_lens:
+        for i in range(q):
+            last = int(L) - q + i
+            if last >= r:
+                vis += (last - r) // W + 1
+    flops = 2.0 * (576 + 512) * H * vis
+    kv_bytes = float(x.local_lens.sum()) * kv_bytes_per_token(x.kv_dtype)
+    rows = x.batch * q * H
+    other = rows * (576 * 2) + rows * (512 * 4 + 4) + float(x.local_lens.sum()) * 4
+    return flops, kv_bytes, kv_bytes + other
+
+
+def cpu_baseline(x, max_requests: int, budget_s: float):
+    """Time the float64 oracle on a bounded sample of requests, scale to the layer."""
+    import torch
+    from oracle import mla_decode_ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    table = x.req_to_token
+    done, t_total = 0, 0.0
+    for b in range(min(max_requests, x.batch)):
+        n = int(x.local_lens[b])
+        slots = table[b, :n].long()
+        pool = x.pool[slots].cpu()
+        sc = None if x.kv_scale is None else x.kv_scale[slots].cpu().numpy()
+        nb = dict(
+            q_nope=x.q_nope[b:b + 1].cpu().view(torch.int16).numpy().view(np.uint16),
+            q_rope=x.q_rope[b:b + 1].cpu().view(torch.int16).numpy().view(np.uint16),
+            pool=(pool.view(torch.int16).numpy().view(np.uint16) if x.kv_dtype == "bf16"
+                  else pool.numpy()),
+        )
+        compact_table = np.arange(n, dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        mla_decode_ref(nb["q_nope"], nb["q_rope"], nb["pool"], sc, compact_table,
+                       np.asarray(x.seq_lens[b:b + 1]), x.q_len, x.softmax_scale, x.kv_dtype,
+                       x.dcp_size, x.dcp_rank)
+        t_total += time.perf_counter() - t0
+        done += 1
+        log(f"  oracle request {b}: {t_total:.1f}s so far")
+        if t_total > budget_s:
+            break
+    per_layer_us = t_total / done * x.batch * 1e6
+    return {"value": per_layer_us, "unit": "us/layer", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {x.batch} requests of the same workload (float64 numpy "
+                      f"oracle, gather + exact dequant + matmul + softmax), scaled by "
+                      f"{x.batch}/{done}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="mtp")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=4)
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--flush-mb", type=int, default=0,
+                    help="write this many MB between steps (outside the events) to evict L2/MALL")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_latent_kv_absorbed_amd as mla
+    from workload import CONFIGS, config_inputs
+
+    dev = torch.device("cuda:0")
+    cfg = WORKLOADS[args.workload]
+    log(f"generating inputs for {CONFIGS[cfg]['name']} on {dev}")
+    x = config_inputs(cfg, device=dev, dcp_rank=3 if cfg == 4 else 0)
+    torch.cuda.synchronize()
+    seq_dev = torch.from_numpy(np.asarray(x.seq_lens, np.int32)).to(dev)
+    desc = mla.make_desc(x.batch, x.q_len, x.num_heads, x.kv_dtype, page_size=x.page_size,
+                         dcp_size=x.dcp_size, dcp_rank=x.dcp_rank)
+    plan = mla.make_plan(desc, x.seq_lens, device=dev)
+    h = plan.header
+    out = torch.empty((x.batch, x.q_len, x.num_heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((x.batch, x.q_len, x.num_heads), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(h["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+    flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev) if args.flush_mb else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mla.decode(plan, x.q_nope, x.q_rope, x.pool, x.kv_scale, x.req_to_token, seq_dev,
+                   x.softmax_scale, workspace=ws, out=out, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        starts[k].record(stream)
+        step()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    t_us = float(np.mean(times_ms) * 1e3)
+
+    flops, kv_bytes, all_bytes = algorithmic_counts(x)
+    tflops = flops / (t_us * 1e-6) / 1e12
+    kv_tbps = kv_bytes / (t_us * 1e-6) / 1e12
+    roofline = {
+        "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+        "kernel": "mla::decode_kernel (+ merge of split requests) per mla_decode call",
+        "flops_per_launch": flops,
+    }
+    if x.q_len == 1 and x.kv_dtype == "bf16" and x.num_heads <= 128:
+        # Below the bf16 ridge (about 312 FLOP/B): HBM bound.
+        bw = all_bytes / (t_us * 1e-6) / 1e12
+        roofline = {"bound": "hbm", "achieved": round(bw * 1e3, 1), "peak": HBM_PEAK_TBPS * 1e3,
+                    "unit": "GB/s", "frac": round(bw / HBM_PEAK_TBPS, 4), "traffic": None,
+                    "kernel": roofline["kernel"], "bytes_per_launch": all_bytes}
+
+    result = {
+        "metric": METRIC,
+        "value": round(t_us, 2),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": CONFIGS[cfg]["name"], "requests": x.batch,
+                   "context": int(max(x.seq_lens)), "q_len": x.q_len, "heads": x.num_heads,
+                   "kv": x.kv_dtype, "page_size": x.page_size, "dcp": [x.dcp_size, x.dcp_rank]},
+        "kv_tb_per_s": round(kv_tbps, 3),
+        "kv_hbm_peak_frac": round(kv_tbps / HBM_PEAK_TBPS, 4),
+        "mfma_bf16_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "step_us_p10_p50_p90": [round(float(np.percentile(times_ms, p)) * 1e3, 2)
+                                for p in (10, 50, 90)],
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "plan": {k: h[k] for k in ("num_wgs", "num_units", "num_parts", "num_split_reqs")},
+        "context_b200_us_per_layer": B200_CONTEXT_US.get(args.workload),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(x, args.cpu_requests, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

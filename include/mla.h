@@ -59,7 +59,13 @@ typedef struct {
   int32_t num_heads;    /* H >= 1 query heads; rows per request M = q_len * H */
   int32_t kv_lora_rank; /* must be 512 */
   int32_t rope_dim;     /* must be 64 */
-  int32_t page_size;    /* informational (>= 1); the table is per token */
+  int32_t page_size;    /* tokens per pool page (>= 1).  When it is a multiple of 32
+                           the kernel reads one table entry per 32 local indices
+                           and assumes that the 32 slots behind it are consecutive
+                           (slot of j = table[j - j % 32] + j % 32), which holds for
+                           any paged layout whose pages are page_size consecutive
+                           slots starting at a multiple of page_size in the local
+                           index.  Otherwise every entry is read. */
   int32_t kv_dtype;     /* mla_kv_dtype */
   int32_t dcp_size;     /* W >= 1 shards; 1 = unsharded */
   int32_t dcp_rank;     /* 0 <= r < W: this pool holds positions p % W == r */
@@ -111,7 +117,7 @@ mla_status mla_decode_plan(const mla_decode_desc* desc, const int32_t* seq_lens_
  *                    Slots outside [0, num_slots) are clamped (no fault, but the
  *                    result is then undefined).
  *   seq_lens:        int32 [B] device copy of the global lengths used to plan.
- *   softmax_scale:   the scale applied to q . k before the exponent.
+ *   softmax_scale:   the scale applied to q . k before the exponent (finite, > 0).
  *   workspace:       device scratch of >= *workspace_bytes from the plan (may
  *                    be NULL when that is 0), 256-byte aligned.
  *   out:             fp32 [B, q_len, H, 512] device output O.

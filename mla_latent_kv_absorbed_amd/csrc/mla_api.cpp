@@ -337,7 +337,7 @@ mla_status mla_decode(const void* plan_host, const void* plan_device, const void
   if (fp8 && (reinterpret_cast<uintptr_t>(kv_scale) & 3u)) return MLA_ERR_INVALID_ARG;
   if (num_slots < 1 || req_to_token_stride < std::max<int64_t>(1, h->max_local))
     return MLA_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   if ((int64_t)workspace_bytes < h->workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (h->workspace_bytes > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
     return MLA_ERR_INVALID_ARG;

@@ -17,16 +17,17 @@
 // transposing ds_read_b64_tr_b16.  Q (144 VGPRs) stays in registers for the
 // whole unit and O (256 values) accumulates in the MFMA accumulators.
 //
-// KV tiles arrive by direct global->LDS DMA (global_load_lds_dwordx4), one
-// tile ahead.  FP8 rows land in a staging buffer and are widened to BF16
-// (exact: every e4m3fn value is a BF16 value) by the workgroup before use;
-// the per-token fp32 scale multiplies the score column and the probability,
-// never the stored element, so K and V stay exact.
+// KV tiles arrive by direct global->LDS DMA (global_load_lds_dwordx4) two
+// (BF16) or three (FP8) tiles ahead.  FP8 tiles stay e4m3fn codes in LDS:
+// every MFMA operand is read as codes and widened to BF16 in registers
+// (exact: every e4m3fn value is a BF16 value), which halves the LDS bytes per
+// MFMA.  The per-token fp32 scale multiplies the score column and the
+// probability, never the stored element, so K and V stay exact.
 //
-// LDS tile layout: 16-byte chunk cc of token t at cc * 512 + 16 * (t ^ 4 *
-// (cc & 3)).  Reading chunk cc of tokens 0..31 (QK operand) and 4-token x
-// 32-byte blocks of 4 chunks (transposed V operand) are both bank-conflict
-// free under this swizzle, and every DMA lane keeps one token per tile.
+// BF16 tile layout: 16-byte chunk cc of token t at cc * 512 + 16 * (t ^ 4 *
+// (cc & 3)); FP8: chunk c at c * 512 + 16 * (t ^ 16 (c & 1)).  Under these
+// swizzles the K reads (one chunk of 32 tokens) and the transposing V reads
+// are bank-conflict free, and every DMA lane keeps one token per tile.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,6 +35,8 @@
 #include "kernels.h"
 #include "plan_layout.h"
 #include "pv_asm.inc"
+#include "qk_asm.inc"
+#include "fp8_asm.inc"
 
 namespace mla {
 
@@ -82,13 +85,14 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* p) {
   return r;
 }
 
-// LDS map of the decode kernel (bytes).
-constexpr int kLdsTile0 = 0;
-constexpr int kLdsTile1 = kTileBf16;
-constexpr int kLdsStage0 = 2 * kTileBf16;
-constexpr int kLdsStage1 = kLdsStage0 + kTileFp8;
-constexpr int kLdsScale = kLdsStage1 + kTileFp8;  // float[4][kTile], indexed by tile & 3
-constexpr int kLdsBf16Total = 2 * kTileBf16;
+// LDS map of the decode kernel (bytes).  BF16: three tiles of BF16 rows (the
+// DMA runs two tiles ahead).  FP8: four tiles of e4m3fn rows (the DMA runs
+// three tiles ahead) and the per-token scales of four tiles.  An FP8 tile
+// keeps the 16-byte chunk c of token t at c * 512 + 16 * (t ^ 16 (c & 1)).
+constexpr int kBf16Tiles = 3;
+constexpr int kLdsBf16Total = kBf16Tiles * kTileBf16;
+constexpr int kFp8Tiles = 4;
+constexpr int kLdsScale = kFp8Tiles * kTileFp8;  // float[4][kTile], by tile & 3
 constexpr int kLdsFp8Total = kLdsScale + 4 * kTile * 4;
 
 // Workgroup barrier that drains this wave's LDS operations only.  Global->LDS
@@ -128,49 +132,41 @@ __device__ __forceinline__ void issue_tile_dma(const uint8_t* row, const float* 
   }
 }
 
-// VMEM instructions one wave issues per tile: BF16 9; FP8 5, 5, 4, 4 + 1 scale.
-// The wait allows one slot load and the next tile's DMA to stay in flight:
-// vmcnt counts in issue order, so the awaited (older) tile has then landed.
+// Wait until the DMA of an older tile has landed while `newer` later tiles'
+// DMA (and, for general tables, `slots` vector slot loads) may stay in flight.
+// vmcnt counts in issue order, so allowing exactly the instructions issued
+// after the awaited tile is enough.  VMEM instructions per tile and wave:
+// BF16 9; FP8 5, 5, 4, 4 rows + the scales on wave 3.
 template <bool kFp8>
-__device__ __forceinline__ void wait_prev_tile_dma(int w) {
-  if constexpr (!kFp8) {
-    wait_vmcnt<10>();
-  } else {
-    if (w == 2) wait_vmcnt<5>(); else wait_vmcnt<6>();
-  }
-}
-
-// Same, when no vector slot load sits between the two tiles' DMA (paged
-// tables read their entry with a scalar load).
-template <bool kFp8>
-__device__ __forceinline__ void wait_prev_tile_dma_noslot(int w) {
-  if constexpr (!kFp8) {
-    wait_vmcnt<9>();
-  } else {
-    if (w == 2) wait_vmcnt<4>(); else wait_vmcnt<5>();
-  }
-}
-
-// Widen a staged FP8 tile into the BF16 tile layout (exact conversion).
-__device__ __forceinline__ void widen_fp8_tile(const LDS_AS uint8_t* stage, LDS_AS uint8_t* tile,
-                                               int tid) {
-#pragma unroll
-  for (int k = 0; k < 9; ++k) {
-    const int u = tid + 256 * k;
-    const int half = u & 1;
-    const int t = (u >> 1) & 31;
-    const int c8 = u >> 6;
-    const u32x2 raw = *(const LDS_AS u32x2*)(stage + (c8 * kTile + t) * 16 + 8 * half);
-    // Two e4m3fn codes -> two packed BF16 per instruction (scale 1: exact).
-    // (Extracting the elements of v_cvt_pk_f32_fp8 and repacking them was
-    // miscompiled: both halves received the first element.)
-    u32x4 o;
-    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, false));
-    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, true));
-    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, false));
-    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, true));
-    const int cc = 2 * c8 + half;
-    *(LDS_AS u32x4*)(tile + cc * kBlock + swz_tok(cc, t) * 16) = o;
+__device__ __forceinline__ void wait_dma(int w, int newer, int slots) {
+  const int per = kFp8 ? (w == 2 ? 4 : 5) : 9;
+  const int n = newer * per + slots;
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 17: wait_vmcnt<17>(); break;
+    case 18: wait_vmcnt<18>(); break;
+    case 19: wait_vmcnt<19>(); break;
+    case 20: wait_vmcnt<20>(); break;
+    case 21: wait_vmcnt<21>(); break;
+    case 22: wait_vmcnt<22>(); break;
+    case 23: wait_vmcnt<23>(); break;
+    default: wait_vmcnt<0>(); break;  // never under-waits
   }
 }
 
@@ -184,53 +180,80 @@ __device__ __forceinline__ void load_tile_scales(const LDS_AS float* sct, int hk
   }
 }
 
+// A copy of v the compiler cannot see through: values derived from it are
+// recomputed where they are used instead of being kept live (or spilled).
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ int64_t clamp_slot(int64_t s, int64_t n) {
   return s < 0 ? 0 : (s >= n ? n - 1 : s);
 }
 
+// K operand of k-step ks from an FP8 tile: 8 codes of chunk ks (16 features),
+// half hk, of this lane's token, widened to 8 BF16 (exact).
+__device__ __forceinline__ bf16x8 k_operand_fp8(const LDS_AS uint8_t* p) {
+  const u32x2 raw = *(const LDS_AS u32x2*)p;
+  u32x4 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, true));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, false));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, true));
+  return __builtin_bit_cast(bf16x8, o);
+}
+
 // S^T[32 tokens x 32 rows] = K . Q^T over the 576 features of one tile.
 //
-// The accumulator is pinned to VGPRs: the O accumulators take all 256 AGPRs
-// and Q takes 144 VGPRs, so this is the only assignment that fits the 512
-// registers of one wave per SIMD, and the compiler does not choose it by
-// itself.  Because the MFMAs are issued from inline asm, the hazards the
-// compiler would otherwise cover are covered here: a few wait states before
-// each block (operands may have just been written by a VALU move), and
-// enough after the last MFMA for its result to be read by VALU instructions.
-// Dependent MFMAs on the same accumulator issue back to back.
-#define MLA_MFMA4(first)                                                           \
-  "v_mfma_f32_32x32x16_bf16 %0, %1, %5, " first "\n\t"                             \
-  "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"                                    \
-  "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"                                    \
-  "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
-
-__device__ __forceinline__ f32x16 qk_tile(const LDS_AS uint8_t* tile, int kbase_e, int kbase_o,
+// The accumulators are pinned to VGPRs: the O accumulators take all 256
+// AGPRs and Q takes 144 VGPRs, so this is the only assignment that fits the
+// 512 registers of one wave per SIMD, and the compiler does not choose it by
+// itself.  Even and odd k-steps go to two independent chains (s0, s1) so that
+// consecutive MFMAs do not wait on each other.  K operands: BF16 tiles hold
+// chunk cc = 2 ks + hk of token t at cc * 512 + 16 (t ^ 4 (cc & 3)); FP8 tiles
+// hold chunk ks at ks * 512 + 16 (t ^ 16 (ks & 1)), half hk at +8.  `ke` /
+// `ko` are the lane's offsets for even / odd k-steps.  Because the MFMAs are
+// issued from inline asm, the hazards the compiler would otherwise cover are
+// covered here: wait states before each group (operands may just have been
+// written by VALU instructions) and after the last MFMA (its result is read
+// by VALU instructions next).
+template <bool kFp8>
+__device__ __forceinline__ f32x16 qk_tile(const LDS_AS uint8_t* tile, int ke, int ko,
                                           const bf16x8* qf) {
-  f32x16 s;
+  f32x16 s0, s1;
 #pragma unroll
   for (int g = 0; g < kKSteps / 4; ++g) {
     const int ks = 4 * g;
-    const bf16x8 k0 = *(const LDS_AS bf16x8*)(tile + kbase_e + 1024 * (ks + 0));
-    const bf16x8 k1 = *(const LDS_AS bf16x8*)(tile + kbase_o + 1024 * (ks + 1));
-    const bf16x8 k2 = *(const LDS_AS bf16x8*)(tile + kbase_e + 1024 * (ks + 2));
-    const bf16x8 k3 = *(const LDS_AS bf16x8*)(tile + kbase_o + 1024 * (ks + 3));
-    if (g == 0) {
-      asm volatile("s_nop 2\n\t" MLA_MFMA4("0")
-                   : "=&v"(s)
-                   : "v"(k0), "v"(k1), "v"(k2), "v"(k3), "v"(qf[ks]), "v"(qf[ks + 1]),
-                     "v"(qf[ks + 2]), "v"(qf[ks + 3]));
+    bf16x8 k0, k1, k2, k3;
+    if constexpr (kFp8) {
+      k0 = k_operand_fp8(tile + ke + 512 * (ks + 0));
+      k1 = k_operand_fp8(tile + ko + 512 * (ks + 1));
+      k2 = k_operand_fp8(tile + ke + 512 * (ks + 2));
+      k3 = k_operand_fp8(tile + ko + 512 * (ks + 3));
     } else {
-      asm volatile("s_nop 2\n\t" MLA_MFMA4("%0")
-                   : "+v"(s)
-                   : "v"(k0), "v"(k1), "v"(k2), "v"(k3), "v"(qf[ks]), "v"(qf[ks + 1]),
-                     "v"(qf[ks + 2]), "v"(qf[ks + 3]));
+      k0 = *(const LDS_AS bf16x8*)(tile + ke + 1024 * (ks + 0));
+      k1 = *(const LDS_AS bf16x8*)(tile + ko + 1024 * (ks + 1));
+      k2 = *(const LDS_AS bf16x8*)(tile + ke + 1024 * (ks + 2));
+      k3 = *(const LDS_AS bf16x8*)(tile + ko + 1024 * (ks + 3));
+    }
+    if (g == 0) {
+      asm volatile(MLA_QK_GROUP_FIRST_ASM
+                   : [s0] "=&v"(s0), [s1] "=&v"(s1)
+                   : [k0] "v"(k0), [k1] "v"(k1), [k2] "v"(k2), [k3] "v"(k3),
+                     [q0] "v"(qf[ks]), [q1] "v"(qf[ks + 1]), [q2] "v"(qf[ks + 2]),
+                     [q3] "v"(qf[ks + 3]));
+    } else {
+      asm volatile(MLA_QK_GROUP_ASM
+                   : [s0] "+v"(s0), [s1] "+v"(s1)
+                   : [k0] "v"(k0), [k1] "v"(k1), [k2] "v"(k2), [k3] "v"(k3),
+                     [q0] "v"(qf[ks]), [q1] "v"(qf[ks + 1]), [q2] "v"(qf[ks + 2]),
+                     [q3] "v"(qf[ks + 3]));
     }
   }
-  // Result consumed by VALU next: wait out the MFMA write latency.
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
-  return s;
+  // Results consumed by VALU next: wait out the MFMA write latency.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+  return s0 + s1;
 }
-#undef MLA_MFMA4
 
 // Wait out the MFMA write latency before the O accumulators are read by
 // VALU instructions (rescale by the lazy max, or the epilogue).
@@ -264,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int n_lane = lane & 31;   // row within the wave / token within a tile
   const int hk = lane >> 5;       // k-half of MFMA operands
   const int M = ph->rows;
@@ -272,23 +295,37 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   const int qlen = ph->q_len;
   const int W = ph->dcp_size;
   const int R = ph->dcp_rank;
-  constexpr int kAhead = kFp8 ? 2 : 1;  // how many tiles the DMA runs ahead
+  constexpr int kAhead = kFp8 ? 3 : 2;  // how many tiles the DMA runs ahead
+  const float tau_raw = kLazyRescale / a.c2;
   constexpr int kRowBytes = kFp8 ? kRow : 2 * kRow;
 
-  // Lane-constant parts of the LDS operand addresses.  QK operand (chunk
-  // cc = 2 ks + hk of token n_lane): the swizzle only depends on ks & 1.
-  const int kbase_e = 512 * hk + 16 * (n_lane ^ (4 * hk));
-  const int kbase_o = 512 * hk + 16 * (n_lane ^ (8 + 4 * hk));
-  // Transposed V operand: in 16-lane group g16 lane 4 krow + cpart addresses
-  // token 16 e + 8 x + 4 hk + krow, features 32 db + 16 (g16 & 1) + 4 cpart.
+  // Lane-constant parts of the LDS operand addresses (see qk_tile for the
+  // K operand).  BF16 V^T (ds_read_b64_tr_b16): in 16-lane group g16, lane
+  // 4 krow + cpart addresses token 16 e + 8 x + 4 hk + krow, features
+  // 32 db + 16 (g16 & 1) + 4 cpart.  FP8 V^T (ds_read_b64_tr_b8): lane
+  // 2 k + c addresses row k = token 16 e + 8 (k / 4) + 4 kg + k % 4 (kg =
+  // g16 / 2), byte half c of features 32 db + 16 (g16 & 1) .. +16.
   const int g16 = lane >> 4;
-  const int krow = (lane & 15) >> 2;
-  const int cpart = lane & 3;
-  const int c3 = 2 * (g16 & 1) + (cpart >> 1);  // (chunk index) & 3
-  const int vbase0 = 512 * c3 + 16 * ((4 * hk + krow) ^ (4 * c3)) + 8 * (cpart & 1);
-  const int vbase1 = 512 * c3 + 16 * ((8 + 4 * hk + krow) ^ (4 * c3)) + 8 * (cpart & 1);
-  // DMA: the token this lane moves, and its first chunk's byte offset in a row.
-  const int dma_tok = kFp8 ? n_lane : (n_lane ^ (((2 * w + hk) & 3) << 2));
+  int ke, ko, va_off, vb_off;
+  if constexpr (!kFp8) {
+    ke = 512 * hk + 16 * (n_lane ^ (4 * hk));
+    ko = 512 * hk + 16 * (n_lane ^ (8 + 4 * hk));
+    const int krow = (lane & 15) >> 2;
+    const int cpart = lane & 3;
+    const int c3 = 2 * (g16 & 1) + (cpart >> 1);  // (chunk index) & 3
+    va_off = 512 * c3 + 16 * ((4 * hk + krow) ^ (4 * c3)) + 8 * (cpart & 1);
+    vb_off = 512 * c3 + 16 * ((8 + 4 * hk + krow) ^ (4 * c3)) + 8 * (cpart & 1);
+  } else {
+    ke = 16 * n_lane + 8 * hk;
+    ko = 16 * (n_lane ^ 16) + 8 * hk;
+    const int fh = g16 & 1, kg = g16 >> 1, k8 = (lane & 15) >> 1, c = lane & 1;
+    const int tok = 8 * (k8 >> 2) + 4 * kg + (k8 & 3);
+    va_off = 512 * fh + 16 * (tok ^ (16 * fh)) + 8 * c;
+    vb_off = 512 * fh + 16 * ((16 + tok) ^ (16 * fh)) + 8 * c;
+  }
+  // DMA: the token this lane moves (chunk parity decides the swizzle), and
+  // its first chunk's byte offset in a row.
+  const int dma_tok = kFp8 ? (n_lane ^ (16 * hk)) : (n_lane ^ (((2 * w + hk) & 3) << 2));
   const int dma_chunk_off = 16 * (2 * w + hk);
 
   const int u_begin = wg_begin[blockIdx.x];
@@ -330,7 +367,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     f32x16 acc_o[16];
 #pragma unroll
     for (int d = 0; d < 16; ++d) acc_o[d] = f32x16{};
-    float m_ref = -INFINITY;  // running max (log2 domain) of this lane's row
+    float m_ref = -INFINITY;  // running max of this lane's row, raw units (q.k [x scale])
     float l_part = 0.f;       // this lane's share of the row sum
 
     const int ntiles = (j1 - j0 + kTile - 1) / kTile;
@@ -352,86 +389,79 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     };
 
     if (ntiles > 0) {
-      // BF16: the DMA of tile it+1 overlaps the compute of tile it.
-      // FP8: the DMA runs two tiles ahead into a staging buffer, and tile
-      // it+1 is widened to BF16 after the P.V product of tile it.
-      LDS_AS uint8_t* dma_buf0 = lds + (kFp8 ? kLdsStage0 : kLdsTile0);
-      LDS_AS uint8_t* dma_buf1 = lds + (kFp8 ? kLdsStage1 : kLdsTile1);
-      LDS_AS float* sc_lds = (LDS_AS float*)(lds + kLdsScale);
-      {
-        const int64_t s0 = lane_slot(slot_raw(0), 0);
-        issue_tile_dma<kFp8>(a.pool + s0 * kRowBytes + dma_chunk_off, a.kv_scale + s0,
-                             dma_buf0, sc_lds, w, lane);
-      }
-      if constexpr (kFp8) {
-        if (ntiles > 1) {
-          const int64_t s1 = lane_slot(slot_raw(1), 1);
-          issue_tile_dma<kFp8>(a.pool + s1 * kRowBytes + dma_chunk_off, a.kv_scale + s1,
-                               dma_buf1, sc_lds + kTile, w, lane);
+      // BF16: the DMA runs kAhead = 2 tiles ahead into three tile buffers.
+      // FP8: the DMA runs kAhead = 3 tiles ahead into four tile buffers.
+      LDS_AS float* sc_lds = (LDS_AS float*)(lds + (kFp8 ? kLdsScale : 0));
+      auto tile_at = [&](int t) -> LDS_AS uint8_t* {
+        return kFp8 ? lds + (t & 3) * kTileFp8 : lds + (t % 3) * kTileBf16;
+      };
+      // Prologue: DMA of tiles 0 .. kAhead-1.
+#pragma unroll
+      for (int t = 0; t < kAhead; ++t) {
+        if (t < ntiles) {
+          const int64_t sl = lane_slot(slot_raw(t), t);
+          issue_tile_dma<kFp8>(a.pool + sl * kRowBytes + dma_chunk_off, a.kv_scale + sl,
+                               tile_at(t), sc_lds + kTile * (t & 3), w, lane);
         }
       }
       int32_t raw_pending = slot_raw(kAhead);  // locates tile it + kAhead
-      if constexpr (kFp8) {
-        if (ntiles > 1) {
-          if constexpr (kPaged) wait_prev_tile_dma_noslot<kFp8>(w);
-          else wait_prev_tile_dma<kFp8>(w);
-        } else {
-          wait_vmcnt<0>();
-        }
-        barrier_lds();
-        widen_fp8_tile(lds + kLdsStage0, lds + kLdsTile0, tid);
-        barrier_lds();
-      }
 
       for (int it = 0; it < ntiles; ++it) {
         // ---- prefetch: table entry of tile it+kAhead+1, DMA of tile it+kAhead.
         // A vector slot load (general tables) must be issued before the DMA:
-        // the vmcnt arithmetic of wait_prev_tile_dma counts it there.
+        // the vmcnt arithmetic of wait_dma counts it there.
         const int32_t raw_later = slot_raw(it + kAhead + 1);
         asm volatile("" ::: "memory");
         if (it + kAhead < ntiles) {
           const int tn = it + kAhead;
-          const int64_t sl = lane_slot(raw_pending, tn);
-          issue_tile_dma<kFp8>(a.pool + sl * kRowBytes + dma_chunk_off, a.kv_scale + sl,
-                               (tn & 1) ? dma_buf1 : dma_buf0, sc_lds + kTile * (tn & 3), w,
-                               lane);
-          if constexpr (kPaged) wait_prev_tile_dma_noslot<kFp8>(w);
-          else wait_prev_tile_dma<kFp8>(w);
-        } else {
-          wait_vmcnt<0>();
+          // DMA lane constants recomputed here rather than kept live.
+          const int tid_o = opaque(tid), hk_o = (tid_o >> 5) & 1, w_o = tid_o >> 6;
+          const int tok_o = kFp8 ? ((tid_o & 31) ^ (16 * hk_o))
+                                 : ((tid_o & 31) ^ (((2 * w_o + hk_o) & 3) << 2));
+          int64_t sl = raw_pending;
+          if constexpr (kPaged) sl += min(tok_o, jlast - (j0 + tn * kTile));
+          sl = clamp_slot(sl, a.num_slots);
+          issue_tile_dma<kFp8>(a.pool + sl * kRowBytes + 16 * (2 * w_o + hk_o), a.kv_scale + sl,
+                               tile_at(tn), sc_lds + kTile * (tn & 3), w, lane);
         }
+        // Tile it must have landed; later tiles may stay in flight.
+        wait_dma<kFp8>(w, min(ntiles - 1, it + kAhead) - it, kPaged ? 0 : kAhead);
         barrier_lds();
 
-        const LDS_AS uint8_t* tile = lds + ((it & 1) ? kLdsTile1 : kLdsTile0);
+        const LDS_AS uint8_t* tile = tile_at(it);
         const int jt = j0 + it * kTile;
 
         // ---- S^T = K . Q^T
-        f32x16 s = qk_tile(tile, kbase_e, kbase_o, qf);
+        f32x16 s = qk_tile<kFp8>(tile, ke, ko, qf);
 
-        // ---- scores -> log2 domain, mask, tile max.
-        // acc index i holds token 8 (i / 4) + 4 hk + (i % 4) of the tile; for
-        // FP8 its scale is read from LDS here and again for P (cheaper than
-        // holding 16 more registers across the rescale).
+        // ---- scores in raw units x = q.k (times the token scale for FP8),
+        // mask, tile max.  acc index i holds token 8 (i / 4) + 4 hk + (i % 4).
         const LDS_AS float* sct = sc_lds + kTile * (it & 3);
         float ksc[16];
-        if constexpr (kFp8) load_tile_scales(sct, hk, ksc);
-        const int lim = jmax - jt;  // tokens m <= lim are visible to this row
-        float mt = -INFINITY;
+        if constexpr (kFp8) {
+          load_tile_scales(sct, hk, ksc);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = 8 * (i >> 2) + 4 * hk + (i & 3);
-          float v = s[i] * (kFp8 ? a.c2 * ksc[i] : a.c2);
-          v = (m <= lim) ? v : -INFINITY;
-          s[i] = v;
-          mt = fmaxf(mt, v);
+          for (int i = 0; i < 16; ++i) s[i] *= ksc[i];
         }
+        const int lim = jmax - jt;  // tokens m <= lim are visible to this row
+        if (__any(lim < kTile - 1)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int m = 8 * (i >> 2) + 4 * hk + (i & 3);
+            s[i] = (m <= lim) ? s[i] : -INFINITY;
+          }
+        }
+        float mt = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
         mt = wave_xor32_max(mt);
 
-        // ---- lazy rescale: only when the max grows by more than 2^8.
-        const bool need = mt > m_ref + kLazyRescale;
+        // ---- lazy rescale: only when the max grows by more than 2^8 in the
+        // exponent (tau_raw = 8 / c2 in raw units).
+        const bool need = mt > m_ref + tau_raw;
         if (__any(need)) {
           const float m_new = need ? mt : m_ref;
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+          const float alpha = need ? __builtin_amdgcn_exp2f((m_ref - m_new) * a.c2) : 1.0f;
           m_ref = m_new;
           l_part *= alpha;
 #pragma unroll
@@ -445,44 +475,46 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
             acc_o[d] = t;
           }
         }
-        const float msafe = (m_ref == -INFINITY) ? 0.f : m_ref;
+        // p = 2^((x - m) c2); a row with nothing visible yet keeps p = 0.
+        const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * a.c2;
 
         // ---- P (fp32 -> bf16), FP8 value scale folded in.
         if constexpr (kFp8) load_tile_scales(sct, hk, ksc);
         bf16x8 pb0, pb1;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = __builtin_amdgcn_exp2f(s[i] - msafe);
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.c2, -mc));
           l_part += e;
           const float pv = kFp8 ? e * ksc[i] : e;
           if (i < 8) pb0[i] = (__bf16)pv; else pb1[i - 8] = (__bf16)pv;
         }
 
         // ---- O^T += V^T . P^T.  For MFMA e, k-slot 8 hk + jj is token
-        // 16 e + 8 (jj / 4) + 4 hk + jj % 4: two transposing reads of 4 tokens
-        // each (lane addresses va / vb), all inside one asm statement.
+        // 16 e + 8 (jj / 4) + 4 hk + jj % 4 (the layout of P above); the V^T
+        // operands are read with transposing LDS loads inside one asm
+        // statement (lane addresses va / vb: token half 0 / 1 for FP8, the two
+        // 4-token runs for BF16).
         {
-          const LDS_AS uint8_t* va = tile + vbase0;
-          const LDS_AS uint8_t* vb = tile + vbase1;
-          asm volatile(MLA_PV_TILE_ASM
-                       : [a0] "+a"(acc_o[0]), [a1] "+a"(acc_o[1]), [a2] "+a"(acc_o[2]),
-                         [a3] "+a"(acc_o[3]), [a4] "+a"(acc_o[4]), [a5] "+a"(acc_o[5]),
-                         [a6] "+a"(acc_o[6]), [a7] "+a"(acc_o[7]), [a8] "+a"(acc_o[8]),
-                         [a9] "+a"(acc_o[9]), [a10] "+a"(acc_o[10]), [a11] "+a"(acc_o[11]),
-                         [a12] "+a"(acc_o[12]), [a13] "+a"(acc_o[13]), [a14] "+a"(acc_o[14]),
-                         [a15] "+a"(acc_o[15])
-                       : [va] "v"(va), [vb] "v"(vb), [p0] "v"(pb0), [p1] "v"(pb1)
-                       : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247",
-                         "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255",
-                         "memory");
+          const LDS_AS uint8_t* va = tile + va_off;
+          const LDS_AS uint8_t* vb = tile + vb_off;
+#define MLA_PV_OPERANDS                                                                   \
+  : [a0] "+a"(acc_o[0]), [a1] "+a"(acc_o[1]), [a2] "+a"(acc_o[2]), [a3] "+a"(acc_o[3]),   \
+    [a4] "+a"(acc_o[4]), [a5] "+a"(acc_o[5]), [a6] "+a"(acc_o[6]), [a7] "+a"(acc_o[7]),   \
+    [a8] "+a"(acc_o[8]), [a9] "+a"(acc_o[9]), [a10] "+a"(acc_o[10]),                     \
+    [a11] "+a"(acc_o[11]), [a12] "+a"(acc_o[12]), [a13] "+a"(acc_o[13]),                 \
+    [a14] "+a"(acc_o[14]), [a15] "+a"(acc_o[15])                                          \
+  : [va] "v"(va), [vb] "v"(vb), [p0] "v"(pb0), [p1] "v"(pb1)                             \
+  : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249",      \
+    "v250", "v251", "v252", "v253", "v254", "v255", "memory"
+          if constexpr (kFp8) {
+            asm volatile(MLA_PV8_TILE_ASM MLA_PV_OPERANDS);
+          } else {
+            asm volatile(MLA_PV_TILE_ASM MLA_PV_OPERANDS);
+          }
+#undef MLA_PV_OPERANDS
         }
 
         raw_pending = raw_later;
-        if constexpr (kFp8) {
-          if (it + 1 < ntiles)
-            widen_fp8_tile(lds + (((it + 1) & 1) ? kLdsStage1 : kLdsStage0),
-                           lds + (((it + 1) & 1) ? kLdsTile1 : kLdsTile0), tid);
-        }
         barrier_lds();
       }
     }
@@ -492,7 +524,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     const float l_row = l_part + __shfl_xor(l_part, 32);
     const bool empty = !(l_row > 0.f);
     const float inv = empty ? 0.f : 1.0f / l_row;
-    const float lse_v = empty ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_row)) * kLn2;
+    const float lse_v =
+        empty ? -INFINITY : (m_ref * a.c2 + __builtin_amdgcn_logf(l_row)) * kLn2;
     if (row_ok) {
       float* obase;
       float* lbase;
