@@ -1,0 +1,574 @@
+"""Generates tile_asm.inc: the tile work of the decode loop as inline-asm
+statements in which LDS reads, FP8 widening, the softmax, global->LDS DMA and
+MFMAs are software-pipelined by hand.
+
+Building blocks of a statement (any combination):
+
+  QK    S^T = K . Q^T of one tile: 36 MFMAs 32x32x16 bf16 (FP8 K widened
+        from e4m3fn codes in registers)
+  PV    O^T += V^T . P^T of one tile: 32 MFMAs (FP8 V^T widened in registers)
+  SM    the online softmax of one tile, given its scores: scale, max, the
+        lazy rescale decision, exponentials, row sum and P packed to BF16
+  DMA   the global->LDS copy of a later tile (row instructions)
+
+Statements (T = BF16 or FP8):
+
+  MLA_QK_T_ASM       QK (first tile of a unit)
+  MLA_FUSED_BF16_ASM QK of tile t+1 and PV of tile t, plus DMA
+  MLA_PV_T_ASM       PV (last tile of a unit)
+  FP8, pipelined one tile deeper so that the softmax runs in the MFMA shadow:
+  MLA_QKSM_FP8_ASM   QK of tile t+1 and SM of tile t, plus DMA (first step)
+  MLA_STEP_FP8_ASM   QK of tile t+1, SM of tile t and PV of tile t-1, plus DMA
+  MLA_SMPV_FP8_ASM   SM of tile t and PV of tile t-1 (last step)
+  MLA_SM_FP8_ASM     SM alone (one-tile units)
+
+QK and PV MFMAs alternate one for one, so the dependent S chain never stalls
+the matrix pipe while PV MFMAs remain, and the VALU and LDS work (widening,
+softmax) issues between MFMAs, in the shadow of the one that is running.  A
+small list scheduler (below) assigns scratch registers in rings, issues each
+LDS read as early as its ring slot allows, waits for it with the exact lgkmcnt
+(LDS operations complete in issue order), keeps every VALU result two
+instructions away from an MFMA that reads it and every transcendental result
+one instruction away from its first reader.
+
+Operand names:
+  %[q0]..%[q35]  Q^T operands (bf16x8) of k-steps 0..35
+  %[s], %[s1]    S^T accumulator chains of the tile being scored (written);
+                 statements with PV put k-steps 33 and 35 in s1, QK-only
+                 statements the odd k-steps
+  %[a0]..%[a15]  O^T accumulators (AGPR f32x16, read-write), pinned by the
+                 caller to a[16 d : 16 d + 15]; MLA_RESCALE_ASM (O *= %[al])
+                 names them a0..a255
+  %[p0], %[p1]   P^T operands (bf16x8) of the two 16-token halves of the tile
+                 whose PV runs
+  %[ke], %[ko]   BF16 K lane addresses (even / odd k-steps); %[kb] FP8
+  %[va], %[vb]   V^T lane addresses of the two token-row sets
+  %[x0]..%[x15]  SM: the 16 scores of this lane (read-write); on return
+                 %[x0]..%[x7] hold P as 8 packed BF16 pairs
+  %[mref], %[lsum]  SM: running max (raw units) and row-sum share (read-write)
+  %[alpha]       SM: factor the O accumulators must be multiplied by (written)
+  %[c2], %[nfm]  SM scalars: softmax_scale * log2(e) and -FLT_MAX
+  %[bpa]         SM: byte address of lane ^ 32 for ds_bpermute_b32
+  %[mon], %[limh], %[ninf]  SM mask: nonzero (scalar) if some token of the
+                 tile lies past a row's last visible index; the last visible
+                 token minus 4 hk (per lane); -inf (scalar)
+  %[sc]          SM, FP8: LDS address of this lane's first 4 token scales
+  %[m0b], %[m0s] DMA: LDS base of this wave's share; scratch SGPR that keeps
+                 M0, which the statement restores; the address operands
+                 appear in the MLA_GLD(offset) macro
+Each statement clobbers its scratch registers (<NAME>_CLOBBERS, the top of the
+VGPR file), VCC and SCC.
+
+K operands.  BF16: k-step ks reads chunk 2 ks + hk (8 features) of the lane's
+token with one ds_read_b128.  FP8: one ds_read_b128 per k-step pair a fetches
+chunk 2 a + hk (16 codes) of the lane's token; k-step 2 a + h uses codes
+8 h .. 8 h + 7, so k-step 2 a + h, half hk covers features 16 (2 a + hk) +
+8 h .. + 8, and the Q operands are loaded in that order.
+
+V^T operand of block db (features 32 db .. +32), token half e.  BF16: two
+ds_read_b64_tr_b16 at %[va] / %[vb] + 2048 db + 256 e.  FP8: one
+ds_read_b64_tr_b8 at (e ? %[vb] : %[va]) + 1024 db, widened in registers.
+
+SM, per lane (16 scores x_i of one query row; token of x_i is
+8 (i / 4) + 4 hk + i % 4): FP8 x_i *= scale_i; m_t = max over the row (the
+other half of the row sits in lane ^ 32); if (m_t - mref) c2 > 8 the running
+max moves to m_t and alpha = 2^((mref - m_t) c2), else alpha = 1; lsum *= alpha;
+e_i = 2^(x_i c2 - m c2) (with m c2 floored at -FLT_MAX, so a row with nothing
+visible yet gives e = 0); lsum += sum e_i; P_i = e_i (FP8: e_i * scale_i),
+packed to BF16 with round-to-nearest-even.
+
+DMA.  Row instruction k (k = 0..3 FP8, 0..8 BF16) moves 16 bytes per lane from
+the lane's row address + 128 k to LDS %[m0b] + 4096 k + 16 lane (the
+immediate offset applies to both addresses, so M0 advances by 4096 - 128).
+
+Run `python gen_tile_asm.py` after editing; the output is committed.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+
+SCRATCH_HI = 255   # rings are allocated downwards from here
+
+
+def v_order():
+    """PV ops (db, e): feature blocks in pairs so that the two MFMAs into
+    one accumulator are never adjacent."""
+    seq = []
+    for p in range(8):
+        for e in (0, 1):
+            for db in (2 * p, 2 * p + 1):
+                seq.append((db, e))
+    return seq
+
+
+class Read:
+    def __init__(self, rid, ring, instrs):
+        self.rid = rid
+        self.ring = ring
+        self.instrs = instrs    # templates; {r} .. {r3} = ring slot registers
+        self.users = []         # stream positions of its consumers
+        self.need = None        # first position that needs the data
+
+
+class Op:
+    def __init__(self, kind, mfma, read, cvt_dw=None, acc=None):
+        self.kind = kind        # "K" or "V"
+        self.acc = acc
+        self.mfma = mfma        # template: {acc} {x} {x3} {c}
+        self.read = read        # rid feeding the A operand
+        self.cvt_dw = cvt_dw    # widened FP8: first dword of the codes in the read
+
+
+class Stream:
+    def __init__(self, rings):
+        self.lines = []
+        self.lgkm = []          # LDS op tags in issue order
+        self.done = -1          # index of the last LDS op known complete
+        self.last_valu = {}     # register -> len(lines) after it was written
+        self.trans_at = {}      # operand text -> len(lines) after a TRANS op wrote it
+        self.base = {}
+        self.rings = rings
+        r = SCRATCH_HI + 1
+        for name, (n, w) in rings.items():
+            r -= n * w
+            self.base[name] = r
+        self.lowest = r
+
+    def reg(self, ring, slot):
+        n, w = self.rings[ring]
+        return self.base[ring] + (slot % n) * w
+
+    def emit(self, line):
+        self.lines.append(line)
+
+    def lds(self, line, tag):
+        self.emit(line)
+        self.lgkm.append(tag)
+
+    def outstanding(self):
+        return len(self.lgkm) - 1 - self.done
+
+    def wait_index(self, last):
+        if last <= self.done:
+            return
+        n = len(self.lgkm) - 1 - last
+        self.emit(f"s_waitcnt lgkmcnt({min(n, 15)})")
+        self.done = last if n <= 15 else len(self.lgkm) - 16
+
+    def wait(self, tag):
+        self.wait_index(max(i for i, t in enumerate(self.lgkm) if t == tag))
+
+
+def sm_program(fp8: bool, sk: int, tmp: int):
+    """The softmax of one tile as a list of (kind, text, reads, writes, tag).
+
+    kind: "valu", "trans" (v_exp_f32), "lds" (an LDS read; tag names it),
+    "wait" (wait for the LDS read `tag`).  reads / writes are operand texts,
+    for the transcendental-result spacing.  sk: base of two 4-register scale
+    slots; tmp: base of 4 temporaries."""
+    x = [f"%[x{i}]" for i in range(16)]
+    t = [f"v{tmp + i}" for i in range(4)]
+    prog = []
+    n_scale_reads = [0]
+
+    def valu(text, reads, writes, kind="valu"):
+        prog.append((kind, text, reads, writes, None))
+
+    def scale_read(c):
+        slot = sk + 4 * (c % 2)
+        tag = ("SC", n_scale_reads[0])
+        n_scale_reads[0] += 1
+        prog.append(("lds", f"ds_read_b128 v[{slot}:{slot + 3}], %[sc] offset:{32 * c}", [], [], tag))
+        return slot, tag
+
+    def scale_pass():
+        # x_i *= scale_i, four tokens per 16-byte read, two reads in flight.
+        pend = {0: scale_read(0), 1: scale_read(1)}
+        for c in range(4):
+            slot, tag = pend[c]
+            prog.append(("wait", "", [], [], tag))
+            for j in range(4):
+                i = 4 * c + j
+                valu(f"v_mul_f32 {x[i]}, {x[i]}, v{slot + j}", [x[i]], [x[i]])
+            if c + 2 < 4:
+                pend[c + 2] = scale_read(c + 2)
+
+    if fp8:
+        scale_pass()
+    # Causal / range mask (only tiles that need it, %[mon] != 0): token
+    # 8 (i / 4) + 4 hk + i % 4 is visible iff 8 (i / 4) + i % 4 <= %[limh].
+    # One block, so that nothing else lands between the branch and its label.
+    # (-inf goes through a VGPR: v_cndmask reads VCC over the constant bus.)
+    block = ["s_cmp_eq_u32 %[mon], 0", "s_cbranch_scc1 88f", f"v_mov_b32 {t[3]}, %[ninf]"]
+    for i in range(16):
+        block.append(f"v_cmp_le_i32 vcc, {8 * (i >> 2) + (i & 3)}, %[limh]")
+        block.append("s_nop 1")  # VALU-written VCC read as a lane mask
+        block.append(f"v_cndmask_b32 {x[i]}, {t[3]}, {x[i]}, vcc")
+    block.append("88:")
+    prog.append(("block", block, list(x), list(x) + ["vcc"], None))
+    # Row max of this lane's 16 scores.
+    valu(f"v_max3_f32 {t[0]}, {x[0]}, {x[1]}, {x[2]}", x[0:3], [t[0]])
+    valu(f"v_max3_f32 {t[1]}, {x[3]}, {x[4]}, {x[5]}", x[3:6], [t[1]])
+    valu(f"v_max3_f32 {t[0]}, {t[0]}, {t[1]}, {x[6]}", [t[0], t[1], x[6]], [t[0]])
+    valu(f"v_max3_f32 {t[1]}, {x[7]}, {x[8]}, {x[9]}", x[7:10], [t[1]])
+    valu(f"v_max3_f32 {t[0]}, {t[0]}, {t[1]}, {x[10]}", [t[0], t[1], x[10]], [t[0]])
+    valu(f"v_max3_f32 {t[1]}, {x[11]}, {x[12]}, {x[13]}", x[11:14], [t[1]])
+    valu(f"v_max3_f32 {t[0]}, {t[0]}, {t[1]}, {x[14]}", [t[0], t[1], x[14]], [t[0]])
+    valu(f"v_max_f32 {t[0]}, {t[0]}, {x[15]}", [t[0], x[15]], [t[0]])
+    # ... and of the other half of the row (lane ^ 32).
+    prog.append(("lds", f"ds_bpermute_b32 {t[1]}, %[bpa], {t[0]}", [t[0]], [], ("BP",)))
+    prog.append(("wait", "", [], [], ("BP",)))
+    valu(f"v_max_f32 {t[0]}, {t[0]}, {t[1]}", [t[0], t[1]], [t[0]])
+    # Lazy rescale: the running max moves only when the tile max exceeds it
+    # by more than 8 in the exponent, (m_t - mref) c2 > 8 (a row with no
+    # visible token yet has mref = -inf and moves as soon as m_t is finite).
+    valu(f"v_sub_f32 {t[1]}, {t[0]}, %[mref]", [t[0], "%[mref]"], [t[1]])
+    valu(f"v_mul_f32 {t[1]}, %[c2], {t[1]}", [t[1]], [t[1]])
+    valu(f"v_cmp_lt_f32 vcc, 8.0, {t[1]}", [t[1]], ["vcc"])
+    valu("s_nop 1", [], [])  # VALU-written VCC read as a lane mask
+    valu(f"v_cndmask_b32 {t[2]}, %[mref], {t[0]}, vcc", [t[0], "%[mref]", "vcc"], [t[2]])
+    valu(f"v_sub_f32 {t[3]}, %[mref], {t[2]}", ["%[mref]", t[2]], [t[3]])
+    valu(f"v_mul_f32 {t[3]}, %[c2], {t[3]}", [t[3]], [t[3]])
+    valu(f"v_exp_f32 {t[3]}, {t[3]}", [t[3]], [t[3]], kind="trans")
+    valu(f"v_mov_b32 %[mref], {t[2]}", [t[2]], ["%[mref]"])
+    valu(f"v_cndmask_b32 %[alpha], 1.0, {t[3]}, vcc", [t[3], "vcc"], ["%[alpha]"])
+    valu(f"v_mul_f32 %[lsum], %[lsum], %[alpha]", ["%[lsum]", "%[alpha]"], ["%[lsum]"])
+    # m c2, floored so that an all-masked row (m = -inf) gives e = 0.
+    valu(f"v_mul_f32 {t[3]}, %[c2], {t[2]}", [t[2]], [t[3]])
+    valu(f"v_max_f32 {t[3]}, %[nfm], {t[3]}", [t[3]], [t[3]])
+    for i in range(16):
+        valu(f"v_fma_f32 {x[i]}, {x[i]}, %[c2], -{t[3]}", [x[i], t[3]], [x[i]])
+    for i in range(16):
+        valu(f"v_exp_f32 {x[i]}, {x[i]}", [x[i]], [x[i]], kind="trans")
+    # Row-sum share: pairwise tree, then into lsum.
+    valu(f"v_add_f32 {t[0]}, {x[0]}, {x[1]}", x[0:2], [t[0]])
+    valu(f"v_add_f32 {t[1]}, {x[2]}, {x[3]}", x[2:4], [t[1]])
+    valu(f"v_add_f32 {t[2]}, {x[4]}, {x[5]}", x[4:6], [t[2]])
+    valu(f"v_add_f32 {t[3]}, {x[6]}, {x[7]}", x[6:8], [t[3]])
+    valu(f"v_add_f32 {t[0]}, {t[0]}, {t[1]}", [t[0], t[1]], [t[0]])
+    valu(f"v_add_f32 {t[2]}, {t[2]}, {t[3]}", [t[2], t[3]], [t[2]])
+    valu(f"v_add_f32 {t[1]}, {x[8]}, {x[9]}", x[8:10], [t[1]])
+    valu(f"v_add_f32 {t[3]}, {x[10]}, {x[11]}", x[10:12], [t[3]])
+    valu(f"v_add_f32 {t[0]}, {t[0]}, {t[2]}", [t[0], t[2]], [t[0]])
+    valu(f"v_add_f32 {t[1]}, {t[1]}, {t[3]}", [t[1], t[3]], [t[1]])
+    valu(f"v_add_f32 {t[2]}, {x[12]}, {x[13]}", x[12:14], [t[2]])
+    valu(f"v_add_f32 {t[3]}, {x[14]}, {x[15]}", x[14:16], [t[3]])
+    valu(f"v_add_f32 {t[0]}, {t[0]}, {t[1]}", [t[0], t[1]], [t[0]])
+    valu(f"v_add_f32 {t[2]}, {t[2]}, {t[3]}", [t[2], t[3]], [t[2]])
+    valu(f"v_add_f32 {t[0]}, {t[0]}, {t[2]}", [t[0], t[2]], [t[0]])
+    valu(f"v_add_f32 %[lsum], %[lsum], {t[0]}", ["%[lsum]", t[0]], ["%[lsum]"])
+    if fp8:
+        scale_pass()   # P_i = e_i * scale_i (the value scale of token i)
+    for j in range(8):
+        valu(f"v_cvt_pk_bf16_f32 {x[j]}, {x[2 * j]}, {x[2 * j + 1]}", [x[2 * j], x[2 * j + 1]], [x[j]])
+    return prog
+
+
+def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
+              tail_chains: int = 2):
+    reads = {}
+    kops, vops = [], []
+    if qk:
+        mf = "v_mfma_f32_32x32x16_bf16 {acc}, v[{x}:{x3}], %[qKS], {c}"
+        if fp8:
+            for a in range(18):
+                reads[("K", a)] = Read(("K", a), "KR",
+                                       [f"ds_read_b128 v[{{r}}:{{r3}}], %[kb] offset:{1024 * a}"])
+            for ks in range(36):
+                kops.append(Op("K", mf.replace("KS", str(ks)), ("K", ks // 2), cvt_dw=2 * (ks % 2)))
+        else:
+            for ks in range(36):
+                base = "%[ke]" if ks % 2 == 0 else "%[ko]"
+                reads[("K", ks)] = Read(("K", ks), "KR",
+                                        [f"ds_read_b128 v[{{r}}:{{r3}}], {base} offset:{1024 * ks}"])
+                kops.append(Op("K", mf.replace("KS", str(ks)), ("K", ks)))
+    if pv:
+        for j, (db, e) in enumerate(v_order()):
+            mfma = f"v_mfma_f32_32x32x16_bf16 %[a{db}], v[{{x}}:{{x3}}], %[p{e}], %[a{db}]"
+            if fp8:
+                base = "%[vb]" if e else "%[va]"
+                reads[("V", j)] = Read(("V", j), "VR",
+                                       [f"ds_read_b64_tr_b8 v[{{r}}:{{r1}}], {base} offset:{1024 * db}"])
+                vops.append(Op("V", mfma, ("V", j), cvt_dw=0, acc=f"a{db}"))
+            else:
+                off = 2048 * db + 256 * e
+                reads[("V", j)] = Read(("V", j), "VR", [
+                    f"ds_read_b64_tr_b16 v[{{r}}:{{r1}}], %[va] offset:{off}",
+                    f"ds_read_b64_tr_b16 v[{{r2}}:{{r3}}], %[vb] offset:{off}"])
+                vops.append(Op("V", mfma, ("V", j), acc=f"a{db}"))
+    # S chains: QK-only statements alternate two chains; with PV one chain
+    # while PV MFMAs separate its steps, and two for the tail.
+    for i, op in enumerate(kops):
+        if not pv:
+            op.acc = "s" if i % 2 == 0 else "s1"
+        else:
+            tail = i - len(vops)
+            op.acc = "s1" if tail_chains == 2 and tail >= 0 and tail % 2 == 1 else "s"
+    ops = []
+    i = j = 0
+    while i < len(kops) or j < len(vops):
+        if i < len(kops):
+            ops.append(kops[i])
+            i += 1
+        if j < len(vops):
+            ops.append(vops[j])
+            j += 1
+    n = len(ops)
+    for p, op in enumerate(ops):
+        rd = reads[op.read]
+        rd.users.append(p)
+        rd.need = p if rd.need is None else min(rd.need, p)
+
+    dma_at = {}
+    for k in range(n_dma):
+        dma_at.setdefault((2 * k + 1) * n // (2 * n_dma), []).append(k)
+
+    rings = {}
+    if qk:
+        rings["KR"] = (3, 4) if fp8 else (5, 4)
+    if pv:
+        rings["VR"] = (4, 2) if fp8 else ((6, 4) if qk else (4, 4))
+    if fp8 and (qk or pv):
+        rings["C"] = (2, 4)
+    if sm:
+        rings["SK"] = (2, 4)
+        rings["ST"] = (1, 4)
+    st = Stream(rings)
+    st.emit("s_nop 2")  # operands may have just been written by VALU instructions
+    if n_dma:
+        st.emit("s_mov_b32 %[m0s], m0")  # M0 is handed back unchanged
+
+    smp = sm_program(fp8, st.base["SK"], st.base["ST"]) if sm else []
+    sm_next = [0]
+
+    queue = {}
+    for rid, rd in sorted(reads.items(), key=lambda kv: kv[1].need):
+        queue.setdefault(rd.ring, []).append(rid)
+    slot_of = {rid: k for q in queue.values() for k, rid in enumerate(q)}
+    nxt = {ring: 0 for ring in queue}
+    issued, freed = set(), set()
+    cvt_slot = {}
+    widened = {}
+    ring_next = {"C": 0}
+    slot_last_user = {}
+    state = {"pos": -1}  # last issued MFMA
+
+    def slot_free(ring):
+        q, k = queue[ring], nxt[ring]
+        size = rings[ring][0]
+        return k < len(q) and (k < size or q[k - size] in freed)
+
+    def budget_ok(ring):
+        return st.outstanding() + len(reads[queue[ring][nxt[ring]]].instrs) <= 13
+
+    def issue(ring):
+        rid = queue[ring][nxt[ring]]
+        nxt[ring] += 1
+        r = st.reg(ring, slot_of[rid])
+        for tmpl in reads[rid].instrs:
+            st.lds(tmpl.format(r=r, r1=r + 1, r2=r + 2, r3=r + 3), rid)
+        issued.add(rid)
+
+    def fill():
+        while True:
+            cands = [g for g in queue if slot_free(g) and budget_ok(g)]
+            if not cands:
+                return
+            cands.sort(key=lambda g: reads[queue[g][nxt[g]]].need)
+            issue(cands[0])
+
+    def ensure(rid):
+        ring = reads[rid].ring
+        while rid not in issued:
+            assert slot_free(ring), f"{rid}: ring {ring} has no free slot"
+            if not budget_ok(ring):
+                st.wait_index(st.done + 1)  # retire the oldest LDS op
+                continue
+            issue(ring)
+        st.wait(rid)
+
+    def release_direct(rid):
+        rd = reads[rid]
+        if rd.ring in ("VR", "KR") and not fp8:
+            if all(u <= state["pos"] - 1 for u in rd.users):
+                freed.add(rid)
+
+    def widen(i):
+        op = ops[i]
+        key = (op.read, op.cvt_dw)
+        if key in widened:
+            cvt_slot[i] = widened[key]
+            return
+        rd = reads[op.read]
+        ensure(op.read)
+        slot = ring_next["C"] % rings["C"][0]
+        ring_next["C"] += 1
+        prev = slot_last_user.get(slot)
+        assert prev is None or prev <= state["pos"] - 1, f"C slot {slot} still read by MFMA {prev}"
+        src = st.reg(rd.ring, slot_of[op.read]) + op.cvt_dw
+        dst = st.reg("C", slot)
+        st.emit(f"v_cvt_scalef32_pk_bf16_fp8 v{dst}, v{src}, 1.0")
+        st.emit(f"v_cvt_scalef32_pk_bf16_fp8 v{dst + 1}, v{src}, 1.0 op_sel:[1,0,0]")
+        st.emit(f"v_cvt_scalef32_pk_bf16_fp8 v{dst + 2}, v{src + 1}, 1.0")
+        st.emit(f"v_cvt_scalef32_pk_bf16_fp8 v{dst + 3}, v{src + 1}, 1.0 op_sel:[1,0,0]")
+        st.last_valu[dst] = len(st.lines)
+        widened[key] = slot
+        cvt_slot[i] = slot
+        slot_last_user[slot] = max(j for j in range(n) if (ops[j].read, ops[j].cvt_dw) == key)
+        if all((ops[u].read, ops[u].cvt_dw) in widened for u in rd.users):
+            freed.add(op.read)
+
+    sm_lds_slot = {}
+
+    def sm_emit(count, slot=None):
+        """Emit up to `count` softmax instructions (waits do not count).  A
+        wait for a softmax LDS read issued less than two MFMA slots ago is
+        deferred to a later slot, so the wave does not stall on it."""
+        done = 0
+        while sm_next[0] < len(smp) and done < count:
+            kind, text, rds, wrs, tag = smp[sm_next[0]]
+            if kind == "wait":
+                if slot is not None and sm_lds_slot.get(tag, -9) > slot - 2:
+                    return
+                sm_next[0] += 1
+                st.wait(tag)
+                continue
+            sm_next[0] += 1
+            # A transcendental result needs one instruction before its reader.
+            for r in rds:
+                at = st.trans_at.get(r)
+                if at is not None and len(st.lines) - at < 1:
+                    st.emit("s_nop 0")
+            if kind == "lds":
+                if st.outstanding() >= 13:
+                    st.wait_index(st.done + 1)
+                st.lds(text, tag)
+                sm_lds_slot[tag] = slot if slot is not None else -9
+            elif kind == "block":
+                for line in text:
+                    st.emit(line)
+            else:
+                st.emit(text)
+            for w in wrs:
+                if kind == "trans":
+                    st.trans_at[w] = len(st.lines)
+                else:
+                    st.trans_at.pop(w, None)
+            done += 1
+
+    n_sm = sum(1 for p in smp if p[0] != "wait")
+    per_slot = math.ceil(n_sm / max(1, n - 2)) if n else n_sm
+
+    started = set()
+    fill()
+    if ops and ops[0].cvt_dw is not None:
+        widen(0)
+    for i, op in enumerate(ops):
+        if op.cvt_dw is not None:
+            if i not in cvt_slot:
+                widen(i)
+            x = st.reg("C", cvt_slot[i])
+            gap = len(st.lines) - st.last_valu[x]
+        else:
+            ensure(op.read)
+            x = st.reg(reads[op.read].ring, slot_of[op.read])
+            gap = 2
+        if gap < 2:
+            st.emit(f"s_nop {1 - gap}")
+        if op.kind == "K":
+            c = f"%[{op.acc}]" if op.acc in started else "0"
+            started.add(op.acc)
+            st.emit(op.mfma.format(acc=f"%[{op.acc}]", x=x, x3=x + 3, c=c))
+        else:
+            st.emit(op.mfma.format(x=x, x3=x + 3))
+        state["pos"] = i
+        if i >= 1:
+            release_direct(ops[i - 1].read)
+        for k in dma_at.get(i, []):
+            st.emit("s_mov_b32 m0, %[m0b]" if k == 0 else "s_add_u32 m0, m0, 3968")
+            st.emit("s_nop 0")
+            st.emit(f"@GLD({128 * k})")
+        if i >= 1:
+            sm_emit(per_slot, i)
+        if i + 1 < n and ops[i + 1].cvt_dw is not None:
+            widen(i + 1)
+        fill()
+    sm_emit(len(smp))
+    for rid in reads:
+        assert rid in issued, f"read {rid} never issued"
+    if sm:
+        st.emit("s_waitcnt lgkmcnt(0)")
+    if n_dma:
+        st.emit("s_mov_b32 m0, %[m0s]")
+    if ops:
+        # S chains are read by VALU code next; O accumulators may be read by
+        # v_accvgpr_read next: wait out the MFMA write latency.
+        st.emit("s_nop 7")
+        st.emit("s_nop 7")
+        st.emit("s_nop 7")
+    elif sm:
+        st.emit("s_nop 1")  # the last results are packed by VALU just above
+    return st.lines, st.lowest
+
+
+def rescale_statement():
+    """O *= alpha: every accumulator register (a0..a255, pinned by the
+    caller's operand constraints) through VGPR temporaries, eight in flight,
+    so that each value is two or more instructions old before it is read."""
+    tmp = list(range(SCRATCH_HI - 7, SCRATCH_HI + 1))
+    lines = ["s_nop 7", "s_nop 7", "s_nop 7"]  # accumulators may just have been written by MFMAs
+    for base in range(0, 256, 8):
+        for k in range(8):
+            lines.append(f"v_accvgpr_read_b32 v{tmp[k]}, a{base + k}")
+        for k in range(8):
+            lines.append(f"v_mul_f32 v{tmp[k]}, %[al], v{tmp[k]}")
+        for k in range(8):
+            lines.append(f"v_accvgpr_write_b32 a{base + k}, v{tmp[k]}")
+    lines.append("s_nop 2")  # accumulators written by VALU, read by MFMAs next
+    return lines, tmp[0]
+
+
+def emit_macro(name: str, lines: list[str]) -> str:
+    parts = []
+    for l in lines:
+        if l.startswith("@GLD("):
+            parts.append(f"    MLA_GLD({l[5:-1]})\n")
+        else:
+            parts.append(f'    "{l}\\n\\t"\n')
+    body = "".join(parts)
+    return f"#define {name} \\\n" + body.rstrip("\n").replace("\n", " \\\n") + "\n"
+
+
+STATEMENTS = (
+    ("MLA_QK_BF16_ASM", dict(fp8=False, qk=True, pv=False)),
+    ("MLA_FUSED_BF16_ASM", dict(fp8=False, qk=True, pv=True, n_dma=9)),
+    ("MLA_PV_BF16_ASM", dict(fp8=False, qk=False, pv=True)),
+    ("MLA_QK_FP8_ASM", dict(fp8=True, qk=True, pv=False)),
+    ("MLA_QKSM_FP8_ASM", dict(fp8=True, qk=True, pv=False, sm=True, n_dma=4)),
+    ("MLA_STEP_FP8_ASM", dict(fp8=True, qk=True, pv=True, sm=True, n_dma=4, tail_chains=1)),
+    ("MLA_SMPV_FP8_ASM", dict(fp8=True, qk=False, pv=True, sm=True)),
+    ("MLA_SM_FP8_ASM", dict(fp8=True, qk=False, pv=False, sm=True)),
+    ("MLA_PV_FP8_ASM", dict(fp8=True, qk=False, pv=True)),
+)
+
+
+def main() -> None:
+    out = ["// Generated by gen_tile_asm.py -- do not edit.\n"]
+    lines, low = rescale_statement()
+    out.append(emit_macro("MLA_RESCALE_ASM", lines))
+    regs = ", ".join(f'"v{r}"' for r in range(low, SCRATCH_HI + 1))
+    out.append(f"// Scratch registers of MLA_RESCALE_ASM.\n#define MLA_RESCALE_CLOBBERS {regs}\n")
+    for name, kw in STATEMENTS:
+        lines, low = statement(**kw)
+        out.append(emit_macro(name, lines))
+        regs = ", ".join(f'"v{r}"' for r in range(low, SCRATCH_HI + 1))
+        out.append(f"// Scratch registers of {name}.\n#define {name[:-4]}_CLOBBERS {regs}, \"memory\"\n")
+    here = os.path.dirname(os.path.abspath(__file__))
+    with open(os.path.join(here, "tile_asm.inc"), "w") as f:
+        f.write("\n".join(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+"""Static checks of the inline-asm statements in the decode kernels.
+
+The compiler sees each statement as one instruction with the operands and
+clobbers it declares, so a statement must (a) declare every register it names
+literally, (b) declare as an output every operand it writes, (c) leave no LDS
+read in flight when it ends (a late return would overwrite a register the
+compiler has since reused), (d) declare SCC / VCC when it writes them and
+(e) give M0 back the value it found.  These checks read the generated
+statements and the call sites in the kernel source; no GPU is needed.
+"""
+
+import os
+import re
+
+import pytest
+
+CSRC = os.path.join(os.path.dirname(__file__), "..", "mla_latent_kv_absorbed_amd", "csrc")
+
+
+def _defines():
+    text = open(os.path.join(CSRC, "tile_asm.inc")).read()
+    defs, cur = {}, None
+    for line in text.splitlines():
+        m = re.match(r"#define (\w+)", line)
+        if m:
+            cur = m.group(1)
+            defs[cur] = line[m.end():] + "\n"
+        elif cur:
+            defs[cur] += line + "\n"
+    return defs
+
+
+DEFS = _defines()
+STATEMENTS = sorted(n for n in DEFS if n.endswith("_ASM"))
+
+
+def _instrs(name):
+    return [x.strip() for x in re.findall(r'"([^"]*)\\n\\t"', DEFS[name])]
+
+
+def _clobbers(name):
+    return DEFS.get(name[: -len("_ASM")] + "_CLOBBERS", "")
+
+
+def _call_sites(name):
+    src = open(os.path.join(CSRC, "mla_kernels.hip")).read()
+    sites = []
+    for m in re.finditer(r"asm volatile\(" + name + r"\b", src):
+        depth, i = 1, m.end()
+        while depth:
+            depth += {"(": 1, ")": -1}.get(src[i], 0)
+            i += 1
+        sites.append(src[m.end():i - 1])
+    return src, sites
+
+
+def _expand(src, text):
+    # Expand the operand-list macros used at call sites.
+    for mac in re.findall(r"\bMLA_\w+_OPERANDS\w*", text):
+        m = re.search(r"#define " + mac + r"\b(.*?)(?<!\\)\n", src, re.S)
+        if m:
+            text = text.replace(mac, m.group(1).replace("\\\n", " "))
+    return text
+
+
+def _split_top(text):
+    # Split an asm argument list at the colons that separate its sections
+    # (not those inside quotes or brackets, as in "+{a[0:15]}").
+    parts, depth, quote, cur = [], 0, False, ""
+    for ch in text:
+        if ch == '"':
+            quote = not quote
+        elif not quote and ch in "([{":
+            depth += 1
+        elif not quote and ch in ")]}":
+            depth -= 1
+        if ch == ":" and not quote and depth == 0:
+            parts.append(cur)
+            cur = ""
+        else:
+            cur += ch
+    parts.append(cur)
+    return parts
+
+
+def _literal_vgprs(text):
+    regs = set()
+    for m in re.finditer(r"(?<![%\w])v\[(\d+):(\d+)\]", text):
+        regs.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    for m in re.finditer(r"(?<![%\w\[])v(\d+)(?![\d:])", text):
+        regs.add(int(m.group(1)))
+    return regs
+
+
+NO_DST = ("ds_write", "global_load_lds", "s_cmp", "s_cbranch", "s_waitcnt", "s_nop",
+          "v_cmp", "s_barrier")
+
+
+def _written_operands(name):
+    out = set()
+    for ins in _instrs(name):
+        if not ins or ins.endswith(":") or ins.startswith(NO_DST):
+            continue
+        parts = ins.split(None, 1)
+        if len(parts) == 2:
+            m = re.match(r"%\[(\w+)\]", parts[1].split(",")[0].strip())
+            if m:
+                out.add(m.group(1))
+    return out
+
+
+def test_statements_found():
+    assert "MLA_STEP_FP8_ASM" in STATEMENTS and "MLA_FUSED_BF16_ASM" in STATEMENTS
+
+
+@pytest.mark.parametrize("name", STATEMENTS)
+def test_literal_registers_are_clobbered(name):
+    text = "".join(_instrs(name))
+    declared = set(int(x) for x in re.findall(r'"v(\d+)"', _clobbers(name)))
+    assert _literal_vgprs(text) <= declared
+    assert not re.search(r"(?<![%\w\[])s(\d+)\b", text), "literal SGPRs are not allowed"
+
+
+@pytest.mark.parametrize("name", STATEMENTS)
+def test_lds_reads_drained(name):
+    pending = []  # LDS operations complete in issue order
+    for ins in _instrs(name):
+        op = ins.split(None, 1)[0] if ins else ""
+        if op.startswith(("ds_read", "ds_bpermute")):
+            pending.append(True)
+        elif op.startswith("ds_write"):
+            pending.append(False)
+        elif op == "s_waitcnt":
+            m = re.search(r"lgkmcnt\((\d+)\)", ins)
+            if m:
+                pending = pending[len(pending) - int(m.group(1)):] if int(m.group(1)) < len(pending) else pending
+    assert not any(pending), "an LDS read is still in flight when the statement ends"
+
+
+@pytest.mark.parametrize("name", STATEMENTS)
+def test_m0_restored(name):
+    ins = _instrs(name)
+    touch = [k for k, i in enumerate(ins) if re.search(r"\bm0\b", i)]
+    writes = [k for k in touch if re.match(r"s_\w+ m0\b", ins[k])]
+    if not writes:
+        assert not any(i.startswith("global_load_lds") for i in ins)
+        return
+    # Saved before M0 is first touched, restored by the last write, and no
+    # DMA (which reads M0) after the restore.
+    assert ins[touch[0]] == "s_mov_b32 %[m0s], m0"
+    assert ins[writes[-1]] == "s_mov_b32 m0, %[m0s]"
+    assert not any(i.startswith("global_load_lds") for i in ins[writes[-1]:])
+
+
+@pytest.mark.parametrize("name", STATEMENTS)
+def test_call_sites_declare_outputs_and_flags(name):
+    src, sites = _call_sites(name)
+    if name == "MLA_QK_BF16_ASM" or name == "MLA_QK_FP8_ASM":
+        assert sites
+    ins = _instrs(name)
+    writes_scc = any(re.match(r"s_(add|sub|cmp|and|or|xor|lshl|lshr)", i) for i in ins)
+    writes_vcc = any(re.match(r"v_cmp\w* vcc", i) for i in ins)
+    for site in sites:
+        site = _expand(src, site)
+        sections = _split_top(site)
+        outputs = sections[1]
+        clob = sections[3] if len(sections) > 3 else ""
+        declared_out = set(re.findall(r"\[(\w+)\]\s*\"[=+]", outputs))
+        missing = _written_operands(name) - declared_out
+        assert not missing, f"operands written but not declared as outputs: {sorted(missing)}"
+        if _clobbers(name):
+            assert name[: -len("_ASM")] + "_CLOBBERS" in clob
+        if writes_scc:
+            assert '"scc"' in clob
+        if writes_vcc:
+            assert '"vcc"' in clob
+        # Outputs written before the last input is read must be early-clobber
+        # (or tied read-write) so that no input shares their register.
+        for op, cons in re.findall(r"\[(\w+)\]\s*\"([=+][^\"]*)\"", outputs):
+            assert cons.startswith("+") or "&" in cons, f"{op} is not early-clobber"
