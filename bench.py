@@ -2,7 +2,10 @@
 """Benchmark of absorbed MLA decode on one MI355X.
 
 One step = one mla_decode call (one MLA layer for the whole batch, including
-the merge of split requests) on inputs already resident in HBM.  The default
+the merge of split requests) on inputs already resident in HBM.  The step is
+enqueued as its two halves (mla_decode_attend, then mla_decode_merge) with an
+event between them, so the decode kernel's own duration is measured live on
+the launch stream; that duration prices the roofline.  The default
 workload is the per-GPU share the pages time their B200 kernels on: 16
 requests x 100000 tokens, q_len 5 (causal among the drafts), 96 heads, FP8
 e4m3fn latent KV with a per-token scale, BF16 queries.
@@ -36,6 +39,41 @@ WORKLOADS = {
     "tiny": 1,      # 2 x {1024, 1536}, q1, h16, bf16
     "dcp8": 4,      # one shard of 128 x 100k over 8 shards, q5, h96, fp8
 }
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the decode kernel's sources (to tell stale counter summaries)."""
+    import hashlib
+    h = hashlib.sha256()
+    for fn in ("mla_kernels.hip", "tile_asm.inc", "kernels.h"):
+        with open(os.path.join(ROOT, "mla_latent_kv_absorbed_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per decode-kernel launch from the committed counter summary.
+
+    profiles/decode_kernel_<workload>_traffic.txt holds FETCH_SIZE and
+    WRITE_SIZE per dispatch from two rocprofv3 --pmc runs of this script,
+    scaled by what the same counters read for a plain copy of known size.
+    Returns None when the summary is missing or was taken on other kernel
+    sources.
+    """
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -115,6 +153,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--flush-mb", type=int, default=0,
                     help="write this many MB between steps (outside the events) to evict L2/MALL")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="before the warmup, run one plain device copy of this many MB (for "
+                         "scaling HBM counters); not timed")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -142,15 +183,36 @@ def main():
     flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev) if args.flush_mb else None
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(mid=None):
         mla.decode(plan, x.q_nope, x.q_rope, x.pool, x.kv_scale, x.req_to_token, seq_dev,
-                   x.softmax_scale, workspace=ws, out=out, lse=lse, stream=stream)
+                   x.softmax_scale, workspace=ws, out=out, lse=lse, stream=stream,
+                   phase="attend")
+        if mid is not None:
+            mid.record(stream)
+        mla.decode(plan, x.q_nope, x.q_rope, x.pool, x.kv_scale, x.req_to_token, seq_dev,
+                   x.softmax_scale, workspace=ws, out=out, lse=lse, stream=stream,
+                   phase="merge")
+
+    if args.copy_calibration_mb:
+        # Plain kernels of known size for scaling HBM counters: a fill that
+        # writes n bytes, then a uint8 -> int16 copy that reads n and writes
+        # 2n (a 256 MB fill between them evicts the source from L2).
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        evict = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.int16, device=dev)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: fill of {n} bytes; copy reading {n} and writing {2 * n} bytes")
+        del src, dst, evict
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -158,28 +220,34 @@ def main():
         if flush is not None:
             flush.zero_()
         starts[k].record(stream)
-        step()
+        step(mids[k])
         ends[k].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     times_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    kern_ms = np.array([s.elapsed_time(m) for s, m in zip(starts, mids)])
     t_us = float(np.mean(times_ms) * 1e3)
+    k_us = float(np.mean(kern_ms) * 1e3)
 
     flops, kv_bytes, all_bytes = algorithmic_counts(x)
     tflops = flops / (t_us * 1e-6) / 1e12
     kv_tbps = kv_bytes / (t_us * 1e-6) / 1e12
+    # Roofline of the dominant kernel (mla::decode_kernel), priced by its own
+    # average duration; the merge of split requests is not in it.
+    k_tflops = flops / (k_us * 1e-6) / 1e12
+    traffic = committed_traffic(args.workload)
     roofline = {
-        "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-        "kernel": "mla::decode_kernel (+ merge of split requests) per mla_decode call",
-        "flops_per_launch": flops,
+        "bound": "mfma", "achieved": round(k_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic": traffic, "kernel": "mla::decode_kernel", "kernel_us": round(k_us, 2),
+        "flops_per_launch": flops, "algorithmic_bytes_per_launch": all_bytes,
     }
     if x.q_len == 1 and x.kv_dtype == "bf16" and x.num_heads <= 128:
         # Below the bf16 ridge (about 312 FLOP/B): HBM bound.
-        bw = all_bytes / (t_us * 1e-6) / 1e12
-        roofline = {"bound": "hbm", "achieved": round(bw * 1e3, 1), "peak": HBM_PEAK_TBPS * 1e3,
-                    "unit": "GB/s", "frac": round(bw / HBM_PEAK_TBPS, 4), "traffic": None,
-                    "kernel": roofline["kernel"], "bytes_per_launch": all_bytes}
+        bw = all_bytes / (k_us * 1e-6) / 1e12
+        roofline.update({"bound": "hbm", "achieved": round(bw * 1e3, 1),
+                         "peak": HBM_PEAK_TBPS * 1e3, "unit": "GB/s",
+                         "frac": round(bw / HBM_PEAK_TBPS, 4)})
 
     result = {
         "metric": METRIC,
@@ -202,6 +270,7 @@ def main():
         "mfma_bf16_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "step_us_p10_p50_p90": [round(float(np.percentile(times_ms, p)) * 1e3, 2)
                                 for p in (10, 50, 90)],
+        "merge_us": round(t_us - k_us, 2),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "plan": {k: h[k] for k in ("num_wgs", "num_units", "num_parts", "num_split_reqs")},
         "context_b200_us_per_layer": B200_CONTEXT_US.get(args.workload),

@@ -137,6 +137,30 @@ mla_status mla_decode(const void* plan_host, const void* plan_device,
                       float* out, float* lse, void* stream);
 
 /*
+ * The two halves of mla_decode, for callers that time them apart or run
+ * other work between them (same arguments, checks and errors as mla_decode).
+ *
+ * mla_decode_attend enqueues only the attention kernel: requests the plan
+ * keeps whole get their final (O, LSE) in out / lse; each piece of a cut
+ * request writes its partial (O, LSE) to the workspace (split KV, merged by
+ * LSE as on the DP16-vs-DP2 page, section "MLA").
+ *
+ * mla_decode_merge enqueues the LSE merge of the cut requests' partials
+ * from the workspace into out / lse (nothing when the plan cuts no request).
+ * It must follow mla_decode_attend with the same plan and workspace on the
+ * same stream (or after it completes); the workspace is read, not written.
+ */
+mla_status mla_decode_attend(const void* plan_host, const void* plan_device,
+                             const void* q_nope_absorbed, const void* q_rope,
+                             const void* kv_pool, const float* kv_scale, int64_t num_slots,
+                             const int32_t* req_to_token, int64_t req_to_token_stride,
+                             const int32_t* seq_lens, float softmax_scale, void* workspace,
+                             size_t workspace_bytes, float* out, float* lse, void* stream);
+mla_status mla_decode_merge(const void* plan_host, const void* plan_device,
+                            const void* workspace, size_t workspace_bytes, float* out,
+                            float* lse, void* stream);
+
+/*
  * Merge num_parts partial results by log-sum-exp (DP16-vs-DP2 page, section
  * "MLA": per-shard (O, LSE) are exchanged and merged, dcp_lse_combine).
  *

@@ -60,6 +60,10 @@ def load_library():
     lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, i64, vp, ctypes.c_float,
                                vp, sz, vp, vp, vp]
     lib.mla_decode.restype = i32
+    lib.mla_decode_attend.argtypes = lib.mla_decode.argtypes
+    lib.mla_decode_attend.restype = i32
+    lib.mla_decode_merge.argtypes = [vp, vp, vp, sz, vp, vp, vp]
+    lib.mla_decode_merge.restype = i32
     lib.mla_lse_combine.argtypes = [vp, vp, i32, i64, vp, vp, vp]
     lib.mla_lse_combine.restype = i32
     lib.mla_status_string.argtypes = [i32]
@@ -170,8 +174,15 @@ def _stream(stream) -> int:
 
 
 def decode(plan: Plan, q_nope, q_rope, kv_pool, kv_scale, req_to_token, seq_lens,
-           softmax_scale: float, workspace=None, out=None, lse=None, stream=None):
-    """mla_decode on torch device tensors; allocates out / lse / workspace if not given."""
+           softmax_scale: float, workspace=None, out=None, lse=None, stream=None,
+           phase: str = "both"):
+    """mla_decode on torch device tensors; allocates out / lse / workspace if not given.
+
+    phase "attend" runs only mla_decode_attend, "merge" only mla_decode_merge
+    (same arguments; the workspace must then be the one the attend call used).
+    """
+    if phase not in ("both", "attend", "merge"):
+        raise MlaError(f"unknown phase {phase!r}")
     import torch
     h = plan.header
     if plan.device is None:
@@ -206,14 +217,20 @@ def decode(plan: Plan, q_nope, q_rope, kv_pool, kv_scale, req_to_token, seq_lens
     ws_bytes = h["workspace_bytes"]
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    st = load_library().mla_decode(
-        plan.host.ctypes.data, _ptr(plan.device), _ptr(q_nope), _ptr(q_rope), _ptr(kv_pool),
-        _ptr(kv_scale if fp8 else None), int(kv_pool.shape[0]), _ptr(req_to_token),
-        int(req_to_token.shape[1]), _ptr(seq_lens), float(softmax_scale), _ptr(workspace),
-        0 if workspace is None else int(workspace.numel() * workspace.element_size()),
-        _ptr(out), _ptr(lse), _stream(stream))
+    ws_given = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    lib = load_library()
+    if phase == "merge":
+        st = lib.mla_decode_merge(plan.host.ctypes.data, _ptr(plan.device), _ptr(workspace),
+                                  ws_given, _ptr(out), _ptr(lse), _stream(stream))
+    else:
+        fn = lib.mla_decode if phase == "both" else lib.mla_decode_attend
+        st = fn(plan.host.ctypes.data, _ptr(plan.device), _ptr(q_nope), _ptr(q_rope),
+                _ptr(kv_pool), _ptr(kv_scale if fp8 else None), int(kv_pool.shape[0]),
+                _ptr(req_to_token), int(req_to_token.shape[1]), _ptr(seq_lens),
+                float(softmax_scale), _ptr(workspace), ws_given, _ptr(out), _ptr(lse),
+                _stream(stream))
     if st != MLA_OK:
-        raise MlaError("mla_decode failed", st)
+        raise MlaError(f"mla_decode ({phase}) failed", st)
     return out, lse
 
 

@@ -317,12 +317,17 @@ mla_status mla_decode_plan(const mla_decode_desc* d, const int32_t* seq_lens_hos
   return MLA_OK;
 }
 
-mla_status mla_decode(const void* plan_host, const void* plan_device, const void* q_nope,
-                      const void* q_rope, const void* kv_pool, const float* kv_scale,
-                      int64_t num_slots, const int32_t* req_to_token,
-                      int64_t req_to_token_stride, const int32_t* seq_lens, float softmax_scale,
-                      void* workspace, size_t workspace_bytes, float* out, float* lse,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks the arguments of a decode call and fills the kernel arguments.
+mla_status decode_args(const void* plan_host, const void* plan_device, const void* q_nope,
+                       const void* q_rope, const void* kv_pool, const float* kv_scale,
+                       int64_t num_slots, const int32_t* req_to_token,
+                       int64_t req_to_token_stride, const int32_t* seq_lens, float softmax_scale,
+                       void* workspace, size_t workspace_bytes, float* out, float* lse,
+                       DecodeArgs* a, const PlanHeader** header) {
   if (!plan_host || !plan_device || !q_nope || !q_rope || !kv_pool || !req_to_token ||
       !seq_lens || !out || !lse)
     return MLA_ERR_INVALID_ARG;
@@ -342,32 +347,81 @@ mla_status mla_decode(const void* plan_host, const void* plan_device, const void
   if (h->workspace_bytes > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
     return MLA_ERR_INVALID_ARG;
 
-  DecodeArgs a{};
-  a.plan = static_cast<const uint8_t*>(plan_device);
-  a.q_nope = static_cast<const uint16_t*>(q_nope);
-  a.q_rope = static_cast<const uint16_t*>(q_rope);
-  a.pool = static_cast<const uint8_t*>(kv_pool);
-  a.kv_scale = kv_scale;
-  a.num_slots = num_slots;
-  a.table = req_to_token;
-  a.table_stride = req_to_token_stride;
-  a.seq_lens = seq_lens;
-  a.c2 = softmax_scale * 1.4426950408889634f;
-  a.out = out;
-  a.lse = lse;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                                  h->ws_lse_offset)
-                       : nullptr;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool paged = (h->page_size % kTile) == 0;
-  if (launch_decode(fp8, paged, h->num_wgs, a, s) != hipSuccess) return MLA_ERR_HIP;
-  if (h->num_split_reqs > 0) {
-    if (launch_merge_split(a.plan, h->num_split_reqs, h->rows, a.ws_o, a.ws_lse, out, lse, s) !=
-        hipSuccess)
-      return MLA_ERR_HIP;
-  }
+  *a = DecodeArgs{};
+  a->plan = static_cast<const uint8_t*>(plan_device);
+  a->q_nope = static_cast<const uint16_t*>(q_nope);
+  a->q_rope = static_cast<const uint16_t*>(q_rope);
+  a->pool = static_cast<const uint8_t*>(kv_pool);
+  a->kv_scale = kv_scale;
+  a->num_slots = num_slots;
+  a->table = req_to_token;
+  a->table_stride = req_to_token_stride;
+  a->seq_lens = seq_lens;
+  a->c2 = softmax_scale * 1.4426950408889634f;
+  a->out = out;
+  a->lse = lse;
+  a->ws_o = static_cast<float*>(workspace);
+  a->ws_lse = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                   h->ws_lse_offset)
+                        : nullptr;
+  *header = h;
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_attend(const void* plan_host, const void* plan_device, const void* q_nope,
+                             const void* q_rope, const void* kv_pool, const float* kv_scale,
+                             int64_t num_slots, const int32_t* req_to_token,
+                             int64_t req_to_token_stride, const int32_t* seq_lens,
+                             float softmax_scale, void* workspace, size_t workspace_bytes,
+                             float* out, float* lse, void* stream) {
+  DecodeArgs a;
+  const PlanHeader* h = nullptr;
+  const mla_status st = decode_args(plan_host, plan_device, q_nope, q_rope, kv_pool, kv_scale,
+                                    num_slots, req_to_token, req_to_token_stride, seq_lens,
+                                    softmax_scale, workspace, workspace_bytes, out, lse, &a, &h);
+  if (st != MLA_OK) return st;
+  const bool fp8 = h->kv_dtype == MLA_KV_FP8_E4M3;
+  const bool paged = (h->page_size % kTile) == 0;
+  if (launch_decode(fp8, paged, h->num_wgs, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status mla_decode_merge(const void* plan_host, const void* plan_device, const void* workspace,
+                            size_t workspace_bytes, float* out, float* lse, void* stream) {
+  if (!plan_host || !plan_device || !out || !lse) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(plan_host) || !aligned16(plan_device) || !aligned16(out) || !aligned16(lse))
+    return MLA_ERR_INVALID_ARG;
+  const PlanHeader* h = static_cast<const PlanHeader*>(plan_host);
+  if (h->magic != kPlanMagic || h->version != kPlanVersion) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)workspace_bytes < h->workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (h->num_split_reqs == 0) return MLA_OK;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MLA_ERR_INVALID_ARG;
+  const float* ws_o = static_cast<const float*>(workspace);
+  const float* ws_lse = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) +
+                                                       h->ws_lse_offset);
+  if (launch_merge_split(static_cast<const uint8_t*>(plan_device), h->num_split_reqs, h->rows,
+                         ws_o, ws_lse, out, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status mla_decode(const void* plan_host, const void* plan_device, const void* q_nope,
+                      const void* q_rope, const void* kv_pool, const float* kv_scale,
+                      int64_t num_slots, const int32_t* req_to_token,
+                      int64_t req_to_token_stride, const int32_t* seq_lens, float softmax_scale,
+                      void* workspace, size_t workspace_bytes, float* out, float* lse,
+                      void* stream) {
+  const mla_status st = mla_decode_attend(plan_host, plan_device, q_nope, q_rope, kv_pool,
+                                          kv_scale, num_slots, req_to_token,
+                                          req_to_token_stride, seq_lens, softmax_scale,
+                                          workspace, workspace_bytes, out, lse, stream);
+  if (st != MLA_OK) return st;
+  return mla_decode_merge(plan_host, plan_device, workspace, workspace_bytes, out, lse, stream);
 }
 
 mla_status mla_lse_combine(const float* part_o, const float* part_lse, int32_t num_parts,

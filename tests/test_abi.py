@@ -31,7 +31,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mla.load_library()
     names = declared_functions()
-    assert {"mla_decode_plan", "mla_decode", "mla_lse_combine"} <= names
+    assert {"mla_decode_plan", "mla_decode", "mla_decode_attend", "mla_decode_merge",
+            "mla_lse_combine"} <= names
     for n in sorted(names):
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
 
@@ -119,6 +120,18 @@ def test_decode_and_combine_reject_bad_arguments_on_host():
     st = lib.mla_decode(p.host.ctypes.data, fake, fake, fake, fake, fake, 10, fake, 1024, fake,
                         ctypes.c_float(float("nan")), fake, 1 << 30, fake, fake, None)
     assert st == -1
+    # the two halves check the same way
+    st = lib.mla_decode_attend(p.host.ctypes.data, fake, fake, fake, fake, None, 10, fake, 1024,
+                               fake, ctypes.c_float(0.1), fake, 1 << 30, fake, fake, None)
+    assert st == -1
+    st = lib.mla_decode_merge(ps.host.ctypes.data, fake, fake, ps.workspace_bytes - 256, fake,
+                              fake, None)
+    assert st == -3
+    st = lib.mla_decode_merge(ps.host.ctypes.data, fake, None, ps.workspace_bytes, fake, fake,
+                              None)
+    assert st == -1
+    assert lib.mla_decode_merge(p.host.ctypes.data, fake, None, 0, fake, fake, None) == 0
+    assert lib.mla_decode_merge(bad.ctypes.data, fake, None, 0, fake, fake, None) == -1
     assert lib.mla_lse_combine(None, None, 0, 10, None, None, None) == -1
     assert lib.mla_lse_combine(fake, fake, 2, 0, fake, fake, None) == 0  # nothing to do
     assert lib.mla_lse_combine(fake + 4, fake, 2, 5, fake, fake, None) == -1

@@ -121,6 +121,25 @@ def test_planner_cuts_match_unsplit(kv):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_attend_then_merge_equals_decode(kv):
+    # The two halves of mla_decode, enqueued apart, give the same bits.
+    x = make_inputs(63, [2000, 77, 900], 5, 48, kv, kv_std=0.1 if kv == "bf16" else 1.0)
+    plans = []
+    o1, l1 = gpu_decode(x, force_splits=3, plan_out=plans)
+    plan = plans[0]
+    g = x.to(DEV)
+    seq = torch.from_numpy(np.asarray(x.seq_lens, np.int32)).to(DEV)
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=DEV)
+    o2 = torch.full_like(o1, float("nan"))
+    l2 = torch.full_like(l1, float("nan"))
+    args = (plan, g.q_nope, g.q_rope, g.pool, g.kv_scale, g.req_to_token, seq, x.softmax_scale)
+    mla.decode(*args, workspace=ws, out=o2, lse=l2, phase="attend")
+    mla.decode(*args, workspace=ws, out=o2, lse=l2, phase="merge")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_dcp_shards_merge_to_full_context(kv):
     full = make_inputs(63, [1500, 700, 9, 8, 5], 5, 32, kv, kv_std=0.1 if kv == "bf16" else 1.0)
     o_full, l_full = oracle(full)
