@@ -92,6 +92,11 @@ import os
 SCRATCH_HI = 255   # rings are allocated downwards from here
 
 
+def fp8_v_order():
+    """FP8 PV ops: feature blocks, each MFMA covering the whole tile."""
+    return list(range(16))
+
+
 def v_order():
     """PV ops (db, e): feature blocks in pairs so that the two MFMAs into
     one accumulator are never adjacent."""
@@ -104,17 +109,19 @@ def v_order():
 
 
 class Read:
-    def __init__(self, rid, ring, instrs):
+    def __init__(self, rid, ring, instrs, widen_inplace=False):
         self.rid = rid
         self.ring = ring
-        self.instrs = instrs    # templates; {r} .. {r3} = ring slot registers
+        self.instrs = instrs    # templates; {r} .. {r7} = ring slot registers
+        self.widen_inplace = widen_inplace  # 16 codes in r4..r7 -> 16 BF16 in r0..r7
         self.users = []         # stream positions of its consumers
         self.need = None        # first position that needs the data
 
 
 class Op:
-    def __init__(self, kind, mfma, read, cvt_dw=None, acc=None):
+    def __init__(self, kind, mfma, read, cvt_dw=None, acc=None, xoff=0):
         self.kind = kind        # "K" or "V"
+        self.xoff = xoff        # first register of the A operand within the read's slot
         self.acc = acc
         self.mfma = mfma        # template: {acc} {x} {x3} {c}
         self.read = read        # rid feeding the A operand
@@ -166,8 +173,8 @@ def sm_program(fp8: bool, sk: int, tmp: int):
 
     kind: "valu", "trans" (v_exp_f32), "lds" (an LDS read; tag names it),
     "wait" (wait for the LDS read `tag`).  reads / writes are operand texts,
-    for the transcendental-result spacing.  sk: base of two 4-register scale
-    slots; tmp: base of 4 temporaries."""
+    for the transcendental-result spacing.  sk: base of a 4-register scale
+    slot; tmp: base of 4 temporaries."""
     x = [f"%[x{i}]" for i in range(16)]
     t = [f"v{tmp + i}" for i in range(4)]
     prog = []
@@ -177,23 +184,20 @@ def sm_program(fp8: bool, sk: int, tmp: int):
         prog.append((kind, text, reads, writes, None))
 
     def scale_read(c):
-        slot = sk + 4 * (c % 2)
         tag = ("SC", n_scale_reads[0])
         n_scale_reads[0] += 1
-        prog.append(("lds", f"ds_read_b128 v[{slot}:{slot + 3}], %[sc] offset:{32 * c}", [], [], tag))
-        return slot, tag
+        prog.append(("lds", f"ds_read_b128 v[{sk}:{sk + 3}], %[sc] offset:{32 * c}", [], [], tag))
+        return sk, tag
 
     def scale_pass():
-        # x_i *= scale_i, four tokens per 16-byte read, two reads in flight.
-        pend = {0: scale_read(0), 1: scale_read(1)}
+        # x_i *= scale_i, four tokens per 16-byte read (one slot: the stream
+        # scheduler defers the wait, so other work covers the latency).
         for c in range(4):
-            slot, tag = pend[c]
+            slot, tag = scale_read(c)
             prog.append(("wait", "", [], [], tag))
             for j in range(4):
                 i = 4 * c + j
                 valu(f"v_mul_f32 {x[i]}, {x[i]}, v{slot + j}", [x[i]], [x[i]])
-            if c + 2 < 4:
-                pend[c + 2] = scale_read(c + 2)
 
     if fp8:
         scale_pass()
@@ -259,10 +263,57 @@ def sm_program(fp8: bool, sk: int, tmp: int):
     valu(f"v_add_f32 {t[2]}, {t[2]}, {t[3]}", [t[2], t[3]], [t[2]])
     valu(f"v_add_f32 {t[0]}, {t[0]}, {t[2]}", [t[0], t[2]], [t[0]])
     valu(f"v_add_f32 %[lsum], %[lsum], {t[0]}", ["%[lsum]", t[0]], ["%[lsum]"])
-    if fp8:
-        scale_pass()   # P_i = e_i * scale_i (the value scale of token i)
-    for j in range(8):
-        valu(f"v_cvt_pk_bf16_f32 {x[j]}, {x[2 * j]}, {x[2 * j + 1]}", [x[2 * j], x[2 * j + 1]], [x[j]])
+    if not fp8:
+        for j in range(8):
+            valu(f"v_cvt_pk_bf16_f32 {x[j]}, {x[2 * j]}, {x[2 * j + 1]}",
+                 [x[2 * j], x[2 * j + 1]], [x[j]])
+        return prog
+    scale_pass()   # P_i = e_i * scale_i (the value scale of token i)
+    # P as two e4m3 terms for the FP8 P.V product, in units of 2^(E - 8)
+    # where 2^E bounds the row's P in this tile (both lanes of the row agree
+    # on E, clamped so that the block-scale code stays in 1..254):
+    # hi_i = rne(P_i / 2^(E-8)), lo_i = rne((P_i - hi_i 2^(E-8)) / 2^(E-8)).
+    # The hi codes of x_{4d..4d+3} end in dword x_d, the lo codes in x_{4+d};
+    # %[psco] = 119 + E, the E8M0 code of 2^(E-8) (the MFMA block scale of
+    # both terms).
+    # Four more temporaries: the scale slot, free after the last scale pass.
+    t4, t5, t6, t7 = (f"v{sk + i}" for i in range(4))
+    valu(f"v_max3_f32 {t[0]}, {x[0]}, {x[1]}, {x[2]}", x[0:3], [t[0]])
+    valu(f"v_max3_f32 {t[1]}, {x[3]}, {x[4]}, {x[5]}", x[3:6], [t[1]])
+    valu(f"v_max3_f32 {t[0]}, {t[0]}, {t[1]}, {x[6]}", [t[0], t[1], x[6]], [t[0]])
+    valu(f"v_max3_f32 {t[1]}, {x[7]}, {x[8]}, {x[9]}", x[7:10], [t[1]])
+    valu(f"v_max3_f32 {t[0]}, {t[0]}, {t[1]}, {x[10]}", [t[0], t[1], x[10]], [t[0]])
+    valu(f"v_max3_f32 {t[1]}, {x[11]}, {x[12]}, {x[13]}", x[11:14], [t[1]])
+    valu(f"v_max3_f32 {t[0]}, {t[0]}, {t[1]}, {x[14]}", [t[0], t[1], x[14]], [t[0]])
+    valu(f"v_max_f32 {t[0]}, {t[0]}, {x[15]}", [t[0], x[15]], [t[0]])
+    prog.append(("lds", f"ds_bpermute_b32 {t[1]}, %[bpa], {t[0]}", [t[0]], [], ("BP2",)))
+    prog.append(("wait", "", [], [], ("BP2",)))
+    valu(f"v_max_f32 {t[0]}, {t[0]}, {t[1]}", [t[0], t[1]], [t[0]])
+    valu(f"v_frexp_exp_i32_f32 {t[1]}, {t[0]}", [t[0]], [t[1]])
+    valu(f"v_max_i32 {t[1]}, 0xffffff8a, {t[1]}", [t[1]], [t[1]])   # E >= -118
+    valu(f"v_min_i32 {t[1]}, 0x87, {t[1]}", [t[1]], [t[1]])         # E <= 135
+    valu(f"v_add_u32 {t[3]}, -8, {t[1]}", [t[1]], [t[3]])
+    valu(f"v_ldexp_f32 {t7}, 1.0, {t[3]}", [t[3]], [t7])
+    valu(f"v_add_u32 %[psco], 0x77, {t[1]}", [t[1]], ["%[psco]"])
+    for d in range(4):
+        a, b, c, e = x[4 * d:4 * d + 4]
+        hi = t4 if d == 0 else x[d]          # x_1..x_3 are free once group 0 is done
+        lo = t5 if d == 0 else x[4 + d]      # x_5..x_7 are free once group 1 is read
+        valu(f"v_cvt_scalef32_pk_fp8_f32 {hi}, {a}, {b}, {t7}", [a, b, t7], [hi])
+        valu(f"v_cvt_scalef32_pk_fp8_f32 {hi}, {c}, {e}, {t7} op_sel:[0,0,0,1]", [c, e, t7], [hi])
+        valu(f"v_cvt_scalef32_pk_f32_fp8 v[{tmp}:{tmp + 1}], {hi}, {t7}", [hi, t7], [t[0], t[1]])
+        valu(f"v_cvt_scalef32_pk_f32_fp8 v[{tmp + 2}:{tmp + 3}], {hi}, {t7} op_sel:[1,0,0]",
+             [hi, t7], [t[2], t[3]])
+        valu(f"v_sub_f32 {a}, {a}, {t[0]}", [a, t[0]], [a])
+        valu(f"v_sub_f32 {b}, {b}, {t[1]}", [b, t[1]], [b])
+        valu(f"v_sub_f32 {c}, {c}, {t[2]}", [c, t[2]], [c])
+        valu(f"v_sub_f32 {e}, {e}, {t[3]}", [e, t[3]], [e])
+        valu(f"v_cvt_scalef32_pk_fp8_f32 {lo}, {a}, {b}, {t7}", [a, b, t7], [lo])
+        valu(f"v_cvt_scalef32_pk_fp8_f32 {lo}, {c}, {e}, {t7} op_sel:[0,0,0,1]", [c, e, t7], [lo])
+        if d == 0:
+            valu(f"v_mov_b32 {x[0]}, {t4}", [t4], [x[0]])
+        if d == 1:
+            valu(f"v_mov_b32 {x[4]}, {t5}", [t5], [x[4]])
     return prog
 
 
@@ -273,11 +324,31 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
     if qk:
         mf = "v_mfma_f32_32x32x16_bf16 {acc}, v[{x}:{x3}], %[qKS], {c}"
         if fp8:
-            for a in range(18):
-                reads[("K", a)] = Read(("K", a), "KR",
-                                       [f"ds_read_b128 v[{{r}}:{{r3}}], %[kb] offset:{1024 * a}"])
-            for ks in range(36):
-                kops.append(Op("K", mf.replace("KS", str(ks)), ("K", ks // 2), cvt_dw=2 * (ks % 2)))
+            # FP8 MFMAs on the stored codes: per 64-feature block kb, lane
+            # half h holds features 64 kb + 16 h + (0..15) in bytes 0..15 and
+            # 64 kb + 32 + 16 h + (0..15) in bytes 16..31 (chunks 4 kb + h and
+            # 4 kb + 2 + h of its token), against the hi and lo e4m3 terms
+            # of Q (%[qhKB], %[qlKB]) with the row's block scale %[qsc].
+            mq = ("v_mfma_scale_f32_32x32x64_f8f6f4 {acc}, v[{x}:{x7}], %[qTKB], {c}, "
+                  "%[s127], %[qsc] op_sel_hi:[0,0,0]")
+            for kb in range(8):
+                reads[("K", kb)] = Read(("K", kb), "KR", [
+                    f"ds_read_b128 v[{{r}}:{{r3}}], %[kb] offset:{2048 * kb}",
+                    f"ds_read_b128 v[{{r4}}:{{r7}}], %[kb] offset:{2048 * kb + 1024}"])
+                for term in ("h", "l"):
+                    kops.append(Op("K", mq.replace("T", term).replace("KB", str(kb)), ("K", kb)))
+            # The RoPE features (512..575) stay on BF16 MFMAs, exact for any
+            # magnitude: read a = 16, 17 fetches chunk 2 a + hk (16 codes,
+            # features 16 (2 a + hk) + 0..15), widened in its own slot;
+            # k-step 2 a + h uses the BF16 features 8 h .. 8 h + 7 of it
+            # against %[qr(2 a + h)].
+            for a in (16, 17):
+                reads[("K", a)] = Read(("K", a), "KR", [
+                    f"ds_read_b128 v[{{r4}}:{{r7}}], %[kb] offset:{1024 * a}"], widen_inplace=True)
+                for h in (0, 1):
+                    ks = 2 * a + h
+                    kops.append(Op("K", mf.replace("%[qKS]", f"%[qr{ks - 32}]"), ("K", a),
+                                   xoff=4 * h))
         else:
             for ks in range(36):
                 base = "%[ke]" if ks % 2 == 0 else "%[ko]"
@@ -285,14 +356,22 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
                                         [f"ds_read_b128 v[{{r}}:{{r3}}], {base} offset:{1024 * ks}"])
                 kops.append(Op("K", mf.replace("KS", str(ks)), ("K", ks)))
     if pv:
-        for j, (db, e) in enumerate(v_order()):
+        if fp8:
+            # One FP8 MFMA per feature block: K = 64 = the tile's 32 tokens
+            # twice, P_hi against the first copy of V^T and P_lo against the
+            # second (bytes 0..15 / 16..31 of every lane).
+            for db in fp8_v_order():
+                mfma = (f"v_mfma_scale_f32_32x32x64_f8f6f4 %[a{db}], v[{{x}}:{{x7}}], %[pp], "
+                        f"%[a{db}], %[s127], %[pscv] op_sel_hi:[0,0,0]")
+                reads[("V", db)] = Read(("V", db), "VR", [
+                    f"ds_read_b64_tr_b8 v[{{r}}:{{r1}}], %[va] offset:{1024 * db}",
+                    f"ds_read_b64_tr_b8 v[{{r2}}:{{r3}}], %[vb] offset:{1024 * db}",
+                    f"ds_read_b64_tr_b8 v[{{r4}}:{{r5}}], %[va] offset:{1024 * db}",
+                    f"ds_read_b64_tr_b8 v[{{r6}}:{{r7}}], %[vb] offset:{1024 * db}"])
+                vops.append(Op("V", mfma, ("V", db), acc=f"a{db}"))
+        for j, (db, e) in enumerate(v_order() if not fp8 else []):
             mfma = f"v_mfma_f32_32x32x16_bf16 %[a{db}], v[{{x}}:{{x3}}], %[p{e}], %[a{db}]"
-            if fp8:
-                base = "%[vb]" if e else "%[va]"
-                reads[("V", j)] = Read(("V", j), "VR",
-                                       [f"ds_read_b64_tr_b8 v[{{r}}:{{r1}}], {base} offset:{1024 * db}"])
-                vops.append(Op("V", mfma, ("V", j), cvt_dw=0, acc=f"a{db}"))
-            else:
+            if True:
                 off = 2048 * db + 256 * e
                 reads[("V", j)] = Read(("V", j), "VR", [
                     f"ds_read_b64_tr_b16 v[{{r}}:{{r1}}], %[va] offset:{off}",
@@ -306,15 +385,17 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
         else:
             tail = i - len(vops)
             op.acc = "s1" if tail_chains == 2 and tail >= 0 and tail % 2 == 1 else "s"
+    # Spread the PV MFMAs evenly between the QK MFMAs (one for one when the
+    # counts match), so the dependent S chain is broken up along the whole
+    # statement.
     ops = []
-    i = j = 0
-    while i < len(kops) or j < len(vops):
-        if i < len(kops):
-            ops.append(kops[i])
-            i += 1
-        if j < len(vops):
+    j = 0
+    for i, kop in enumerate(kops):
+        ops.append(kop)
+        while j < len(vops) and (j + 1) * len(kops) <= (i + 1) * len(vops) + len(kops) // 2:
             ops.append(vops[j])
             j += 1
+    ops.extend(vops[j:])
     n = len(ops)
     for p, op in enumerate(ops):
         rd = reads[op.read]
@@ -327,13 +408,11 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
 
     rings = {}
     if qk:
-        rings["KR"] = (3, 4) if fp8 else (5, 4)
+        rings["KR"] = (2, 8) if fp8 else (5, 4)
     if pv:
-        rings["VR"] = (4, 2) if fp8 else ((6, 4) if qk else (4, 4))
-    if fp8 and (qk or pv):
-        rings["C"] = (2, 4)
+        rings["VR"] = (2, 8) if fp8 else ((6, 4) if qk else (4, 4))
     if sm:
-        rings["SK"] = (2, 4)
+        rings["SK"] = (1, 4)
         rings["ST"] = (1, 4)
     st = Stream(rings)
     st.emit("s_nop 2")  # operands may have just been written by VALU instructions
@@ -368,7 +447,8 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
         nxt[ring] += 1
         r = st.reg(ring, slot_of[rid])
         for tmpl in reads[rid].instrs:
-            st.lds(tmpl.format(r=r, r1=r + 1, r2=r + 2, r3=r + 3), rid)
+            st.lds(tmpl.format(r=r, r1=r + 1, r2=r + 2, r3=r + 3, r4=r + 4, r5=r + 5,
+                               r6=r + 6, r7=r + 7), rid)
         issued.add(rid)
 
     def fill():
@@ -379,6 +459,8 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
             cands.sort(key=lambda g: reads[queue[g][nxt[g]]].need)
             issue(cands[0])
 
+    widened_inplace = set()
+
     def ensure(rid):
         ring = reads[rid].ring
         while rid not in issued:
@@ -388,10 +470,21 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
                 continue
             issue(ring)
         st.wait(rid)
+        if reads[rid].widen_inplace and rid not in widened_inplace:
+            # codes in r4..r7 -> BF16 in r0..r7, each source dword read
+            # before the pair that overwrites it
+            r = st.reg(ring, slot_of[rid])
+            for d in range(4):
+                src = r + 4 + d
+                st.emit(f"v_cvt_scalef32_pk_bf16_fp8 v{r + 2 * d}, v{src}, 1.0")
+                st.emit(f"v_cvt_scalef32_pk_bf16_fp8 v{r + 2 * d + 1}, v{src}, 1.0 op_sel:[1,0,0]")
+            st.last_valu[r] = len(st.lines)
+            st.last_valu[r + 4] = len(st.lines)
+            widened_inplace.add(rid)
 
     def release_direct(rid):
         rd = reads[rid]
-        if rd.ring in ("VR", "KR") and not fp8:
+        if all(ops[u].cvt_dw is None for u in rd.users):  # in-place widening included
             if all(u <= state["pos"] - 1 for u in rd.users):
                 freed.add(rid)
 
@@ -473,16 +566,16 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
             gap = len(st.lines) - st.last_valu[x]
         else:
             ensure(op.read)
-            x = st.reg(reads[op.read].ring, slot_of[op.read])
-            gap = 2
+            x = st.reg(reads[op.read].ring, slot_of[op.read]) + op.xoff
+            gap = len(st.lines) - st.last_valu[x] if x in st.last_valu else 2
         if gap < 2:
             st.emit(f"s_nop {1 - gap}")
         if op.kind == "K":
             c = f"%[{op.acc}]" if op.acc in started else "0"
             started.add(op.acc)
-            st.emit(op.mfma.format(acc=f"%[{op.acc}]", x=x, x3=x + 3, c=c))
+            st.emit(op.mfma.format(acc=f"%[{op.acc}]", x=x, x3=x + 3, x7=x + 7, c=c))
         else:
-            st.emit(op.mfma.format(x=x, x3=x + 3))
+            st.emit(op.mfma.format(x=x, x3=x + 3, x7=x + 7))
         state["pos"] = i
         if i >= 1:
             release_direct(ops[i - 1].read)
