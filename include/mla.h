@@ -109,7 +109,8 @@ mla_status mla_decode_plan(const mla_decode_desc* desc, const int32_t* seq_lens_
  *   q_nope_absorbed: bf16 [B, q_len, H, 512], contiguous, device.
  *   q_rope:          bf16 [B, q_len, H, 64], contiguous, device.
  *   kv_pool:         [num_slots, 576] contiguous, device; bf16 or e4m3fn bytes
- *                    per desc.kv_dtype; row = [c_kv (512) | k_rope (64)].
+ *                    per desc.kv_dtype; row = [c_kv (512) | k_rope (64)];
+ *                    1 <= num_slots <= 2^31 - 1.
  *   kv_scale:        fp32 [num_slots] for FP8 (value = e4m3fn(code) * scale),
  *                    NULL for BF16.
  *   req_to_token:    int32 [B, req_to_token_stride], device; column j holds the

@@ -340,7 +340,8 @@ mla_status decode_args(const void* plan_host, const void* plan_device, const voi
                         (const void*)seq_lens, (const void*)out, (const void*)lse})
     if (!aligned16(p)) return MLA_ERR_INVALID_ARG;
   if (fp8 && (reinterpret_cast<uintptr_t>(kv_scale) & 3u)) return MLA_ERR_INVALID_ARG;
-  if (num_slots < 1 || req_to_token_stride < std::max<int64_t>(1, h->max_local))
+  if (num_slots < 1 || num_slots > INT32_MAX ||
+      req_to_token_stride < std::max<int64_t>(1, h->max_local))
     return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   if ((int64_t)workspace_bytes < h->workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;

@@ -112,6 +112,10 @@ def test_decode_and_combine_reject_bad_arguments_on_host():
     st = lib.mla_decode(ps.host.ctypes.data, fake, fake, fake, fake, fake, 10, fake, 1024, fake,
                         ctypes.c_float(0.1), fake, ps.workspace_bytes - 256, fake, fake, None)
     assert st == -3
+    # pools of 2^31 slots or more are rejected (32-bit slot arithmetic)
+    st = lib.mla_decode(p.host.ctypes.data, fake, fake, fake, fake, fake, 1 << 31, fake, 1024,
+                        fake, ctypes.c_float(0.1), fake, 1 << 30, fake, fake, None)
+    assert st == -1
     # FP8 without scales
     st = lib.mla_decode(p.host.ctypes.data, fake, fake, fake, fake, None, 10, fake, 1024, fake,
                         ctypes.c_float(0.1), fake, 1 << 30, fake, fake, None)
