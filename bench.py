@@ -142,6 +142,68 @@ def cpu_baseline(x, max_requests: int, budget_s: float):
                       f"{x.batch}/{done}"}
 
 
+def time_decode(x, dev, steps: int, warmup: int) -> float:
+    """Mean us of mla_decode (attend + merge) on resident inputs, HIP events on the stream."""
+    import torch
+    import mla_latent_kv_absorbed_amd as mla
+    seq_dev = torch.from_numpy(np.asarray(x.seq_lens, np.int32)).to(dev)
+    desc = mla.make_desc(x.batch, x.q_len, x.num_heads, x.kv_dtype, page_size=x.page_size,
+                         dcp_size=x.dcp_size, dcp_rank=x.dcp_rank)
+    plan = mla.make_plan(desc, x.seq_lens, device=dev)
+    ws = torch.zeros(max(plan.header["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((x.batch, x.q_len, x.num_heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((x.batch, x.q_len, x.num_heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mla.decode(plan, x.q_nope, x.q_rope, x.pool, x.kv_scale, x.req_to_token, seq_dev,
+                   x.softmax_scale, workspace=ws, out=out, lse=lse, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]) * 1e3)
+
+
+def run_sweep(args, dev):
+    """Batch sweep at 200k tokens, q_len 5, 96 heads, FP8: e(B) = t_floor(B) / t(B).
+
+    t_floor is the bf16-MFMA time of the algorithmic FLOPs at the vendor peak;
+    no cliff means e(B) varies little over B = 1..24 and t(B) never drops as
+    B grows.
+    """
+    import torch
+    from workload import SWEEP_BATCHES, config_inputs
+    rows = []
+    for B in list(SWEEP_BATCHES) + ["ragged64"]:
+        x = (config_inputs(5, device=dev, ragged=True) if B == "ragged64"
+             else config_inputs(5, device=dev, batch=B))
+        torch.cuda.synchronize()
+        t_us = time_decode(x, dev, args.steps, args.warmup)
+        flops, kv_bytes, _ = algorithmic_counts(x)
+        t_floor = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6
+        rows.append({"batch": B, "tokens": int(np.sum(x.seq_lens)), "us_per_layer": round(t_us, 1),
+                     "kv_tb_per_s": round(kv_bytes / (t_us * 1e-6) / 1e12, 3),
+                     "e": round(t_floor / t_us, 4)})
+        log(f"  sweep {B}: {t_us:.1f} us  e={t_floor / t_us:.3f}")
+        del x
+        torch.cuda.empty_cache()
+    fixed = [r for r in rows if r["batch"] != "ragged64"]
+    es = [r["e"] for r in fixed]
+    ts = [r["us_per_layer"] for r in fixed]
+    print(json.dumps({"sweep": "200k-q5-h96-fp8", "rows": rows,
+                      "e_spread": round(max(es) - min(es), 4),
+                      "t_non_decreasing": all(b >= a for a, b in zip(ts, ts[1:])),
+                      "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +215,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--flush-mb", type=int, default=0,
                     help="write this many MB between steps (outside the events) to evict L2/MALL")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the one-line step benchmark: time the batch sweep at "
+                         "200k tokens (B in 1..24, and the ragged 64-request batch) and "
+                         "print its efficiency spread as one JSON object")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before the warmup, run one plain device copy of this many MB (for "
                          "scaling HBM counters); not timed")
@@ -168,6 +234,9 @@ def main():
     from workload import CONFIGS, config_inputs
 
     dev = torch.device("cuda:0")
+    if args.sweep:
+        run_sweep(args, dev)
+        return
     cfg = WORKLOADS[args.workload]
     log(f"generating inputs for {CONFIGS[cfg]['name']} on {dev}")
     x = config_inputs(cfg, device=dev, dcp_rank=3 if cfg == 4 else 0)
