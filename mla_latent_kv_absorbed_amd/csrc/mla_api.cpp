@@ -433,7 +433,7 @@ mla_status mla_lse_combine(const float* part_o, const float* part_lse, int32_t n
   if (!aligned16(part_o) || !aligned16(out) || (reinterpret_cast<uintptr_t>(part_lse) & 3u) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u))
     return MLA_ERR_INVALID_ARG;
-  if ((rows + 3) / 4 > (int64_t)INT32_MAX) return MLA_ERR_INVALID_ARG;
+  if (rows > (int64_t)INT32_MAX) return MLA_ERR_INVALID_ARG;
   if (launch_lse_combine(part_o, part_lse, num_parts, rows, out, lse,
                          static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
