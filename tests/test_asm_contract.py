@@ -178,3 +178,43 @@ def test_call_sites_declare_outputs_and_flags(name):
         # (or tied read-write) so that no input shares their register.
         for op, cons in re.findall(r"\[(\w+)\]\s*\"([=+][^\"]*)\"", outputs):
             assert cons.startswith("+") or "&" in cons, f"{op} is not early-clobber"
+
+
+# ---------------------------------------------------------------- compiled loops
+
+def _compiled_asm(tmp_path_factory):
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "k.s"
+    inc = os.path.join(os.path.dirname(__file__), "..", "include")
+    subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", inc,
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                    "--cuda-device-only", "-S", os.path.join(CSRC, "mla_kernels.hip"),
+                    "-o", str(out)], check=True, capture_output=True)
+    return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def compiled(tmp_path_factory):
+    return _compiled_asm(tmp_path_factory)
+
+
+@pytest.mark.parametrize("variant", ["ILb1ELb1E", "ILb1ELb0E", "ILb0ELb1E", "ILb0ELb0E"])
+def test_tile_loops_do_not_spill(compiled, variant):
+    # A scratch reload inside a tile loop is a VMEM load: waiting for it also
+    # waits for every global->LDS DMA issued before it, which serialises the
+    # prefetch pipeline.  The innermost loops of every decode variant must be
+    # free of scratch accesses.
+    sym = f"_ZN3mla13decode_kernel{variant}EEvNS_10DecodeArgsE:"
+    start = compiled.index(sym)
+    body = compiled[start:compiled.index(".Lfunc_end", start)].splitlines()
+    headers = [i for i, l in enumerate(body) if "Inner Loop Header" in l]
+    assert headers, "no inner loop found"
+    for h in headers:
+        label = body[h - 1].split(":")[0]
+        ends = [i for i, l in enumerate(body) if label in l and "branch" in l and i > h]
+        seg = body[h:max(ends) + 1]
+        assert not any("scratch_" in l for l in seg), f"spill in loop {label}"
