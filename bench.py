@@ -204,6 +204,76 @@ def run_sweep(args, dev):
                       "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
+def run_dcp_full(args, dev):
+    """All 8 DCP shards of 128 x 100k (q_len 5, 96 heads, FP8) on this GPU, then
+    mla_lse_combine of their (O, LSE) into the full-context result.
+
+    Each shard call writes its (O, LSE) into slot r of a stacked [8, rows, 512]
+    buffer, which is exactly the combine's input layout.
+    """
+    import torch
+    import mla_latent_kv_absorbed_amd as mla
+    from workload import config_inputs
+    W = 8
+    shards, plans = [], []
+    for r in range(W):
+        x = config_inputs(4, device=dev, dcp_rank=r)
+        desc = mla.make_desc(x.batch, x.q_len, x.num_heads, x.kv_dtype, page_size=x.page_size,
+                             dcp_size=x.dcp_size, dcp_rank=x.dcp_rank)
+        plans.append(mla.make_plan(desc, x.seq_lens, device=dev))
+        shards.append(x)
+        log(f"  shard {r} ready")
+    x0 = shards[0]
+    rows = x0.batch * x0.q_len * x0.num_heads
+    part_o = torch.empty((W, rows, 512), dtype=torch.float32, device=dev)
+    part_lse = torch.empty((W, rows), dtype=torch.float32, device=dev)
+    out = torch.empty((rows, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    seq_dev = torch.from_numpy(np.asarray(x0.seq_lens, np.int32)).to(dev)
+    wss = [torch.zeros(max(p.header["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+           for p in plans]
+    stream = torch.cuda.current_stream(dev)
+
+    def shard(r):
+        x = shards[r]
+        mla.decode(plans[r], x.q_nope, x.q_rope, x.pool, x.kv_scale, x.req_to_token, seq_dev,
+                   x.softmax_scale, workspace=wss[r], out=part_o[r].view(x.batch, x.q_len,
+                                                                         x.num_heads, 512),
+                   lse=part_lse[r].view(x.batch, x.q_len, x.num_heads), stream=stream)
+
+    def combine():
+        mla.lse_combine(part_o, part_lse, out=out, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        for r in range(W):
+            shard(r)
+        combine()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(W + 2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        for r in range(W):
+            shard(r)
+            ev[k][r + 1].record(stream)
+        combine()
+        ev[k][W + 1].record(stream)
+    torch.cuda.synchronize()
+    per_shard = np.array([[ev[k][r].elapsed_time(ev[k][r + 1]) for r in range(W)]
+                          for k in range(args.steps)]) * 1e3
+    comb = np.array([ev[k][W].elapsed_time(ev[k][W + 1]) for k in range(args.steps)]) * 1e3
+    total = np.array([ev[k][0].elapsed_time(ev[k][W + 1]) for k in range(args.steps)]) * 1e3
+    comb_bytes = (W + 1) * rows * (512 * 4 + 4)
+    print(json.dumps({
+        "dcp": "128x100k-q5-h96-fp8 over 8 shards (p % 8 == r), all on one GPU",
+        "per_shard_us_median": round(float(np.median(per_shard)), 1),
+        "per_shard_us_by_rank": [round(float(v), 1) for v in np.median(per_shard, axis=0)],
+        "sum_8_shards_plus_combine_us": round(float(np.median(total)), 1),
+        "combine_us": round(float(np.median(comb)), 1),
+        "combine_hbm_tb_per_s": round(comb_bytes / (float(np.median(comb)) * 1e-6) / 1e12, 3),
+        "context_b200_us": {"per_shard_attn_mqa": 826.0, "dcp_pack_plus_lse_combine": 30.0},
+        "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +289,10 @@ def main():
                     help="instead of the one-line step benchmark: time the batch sweep at "
                          "200k tokens (B in 1..24, and the ragged 64-request batch) and "
                          "print its efficiency spread as one JSON object")
+    ap.add_argument("--dcp-full", action="store_true",
+                    help="instead of the one-line step benchmark: run all 8 shards of the DCP "
+                         "workload plus mla_lse_combine, and print per-shard, sum and "
+                         "combine times as one JSON object")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before the warmup, run one plain device copy of this many MB (for "
                          "scaling HBM counters); not timed")
@@ -236,6 +310,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.sweep:
         run_sweep(args, dev)
+        return
+    if args.dcp_full:
+        run_dcp_full(args, dev)
         return
     cfg = WORKLOADS[args.workload]
     log(f"generating inputs for {CONFIGS[cfg]['name']} on {dev}")
