@@ -109,11 +109,12 @@ def v_order():
 
 
 class Read:
-    def __init__(self, rid, ring, instrs, widen_inplace=False):
+    def __init__(self, rid, ring, instrs, widen_inplace=False, dup_half=False):
         self.rid = rid
         self.ring = ring
         self.instrs = instrs    # templates; {r} .. {r7} = ring slot registers
         self.widen_inplace = widen_inplace  # 16 codes in r4..r7 -> 16 BF16 in r0..r7
+        self.dup_half = dup_half            # r4..r7 = copy of r0..r3
         self.users = []         # stream positions of its consumers
         self.need = None        # first position that needs the data
 
@@ -363,11 +364,12 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
             for db in fp8_v_order():
                 mfma = (f"v_mfma_scale_f32_32x32x64_f8f6f4 %[a{db}], v[{{x}}:{{x7}}], %[pp], "
                         f"%[a{db}], %[s127], %[pscv] op_sel_hi:[0,0,0]")
+                # V^T of the 32 tokens is read once (r0..r3) and copied to
+                # r4..r7 by VALU, which halves the LDS traffic of P.V.
                 reads[("V", db)] = Read(("V", db), "VR", [
                     f"ds_read_b64_tr_b8 v[{{r}}:{{r1}}], %[va] offset:{1024 * db}",
-                    f"ds_read_b64_tr_b8 v[{{r2}}:{{r3}}], %[vb] offset:{1024 * db}",
-                    f"ds_read_b64_tr_b8 v[{{r4}}:{{r5}}], %[va] offset:{1024 * db}",
-                    f"ds_read_b64_tr_b8 v[{{r6}}:{{r7}}], %[vb] offset:{1024 * db}"])
+                    f"ds_read_b64_tr_b8 v[{{r2}}:{{r3}}], %[vb] offset:{1024 * db}"],
+                    dup_half=True)
                 vops.append(Op("V", mfma, ("V", db), acc=f"a{db}"))
         for j, (db, e) in enumerate(v_order() if not fp8 else []):
             mfma = f"v_mfma_f32_32x32x16_bf16 %[a{db}], v[{{x}}:{{x3}}], %[p{e}], %[a{db}]"
@@ -470,6 +472,12 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
                 continue
             issue(ring)
         st.wait(rid)
+        if reads[rid].dup_half and rid not in widened_inplace:
+            r = st.reg(ring, slot_of[rid])
+            st.emit(f"v_mov_b64 v[{r + 4}:{r + 5}], v[{r}:{r + 1}]")
+            st.emit(f"v_mov_b64 v[{r + 6}:{r + 7}], v[{r + 2}:{r + 3}]")
+            st.last_valu[r] = len(st.lines)
+            widened_inplace.add(rid)
         if reads[rid].widen_inplace and rid not in widened_inplace:
             # codes in r4..r7 -> BF16 in r0..r7, each source dword read
             # before the pair that overwrites it
