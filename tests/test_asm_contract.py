@@ -202,19 +202,49 @@ def compiled(tmp_path_factory):
     return _compiled_asm(tmp_path_factory)
 
 
+LABEL = re.compile(r"^(\.LBB\w+|; %bb\.\d+):")
+
+
+def _blocks_with_depth(body):
+    # Split a function's assembly into basic blocks, each with the loop depth
+    # the compiler annotates on its label line and the comment lines right
+    # after it (0 outside loops).
+    blocks = []
+    for line in body:
+        if LABEL.match(line):
+            blocks.append({"depth": 0, "lines": [], "head": True})
+        if not blocks:
+            continue
+        blk = blocks[-1]
+        if blk["head"] and (LABEL.match(line) or line.strip().startswith(";")):
+            blk["depth"] = max([blk["depth"]] + [int(x) for x in re.findall(r"Depth=(\d+)", line)])
+        else:
+            blk["head"] = False
+        blk["lines"].append(line)
+    return blocks
+
+
 @pytest.mark.parametrize("variant", ["ILb1ELb1E", "ILb1ELb0E", "ILb0ELb1E", "ILb0ELb0E"])
 def test_tile_loops_do_not_spill(compiled, variant):
     # A scratch reload inside a tile loop is a VMEM load: waiting for it also
     # waits for every global->LDS DMA issued before it, which serialises the
-    # prefetch pipeline.  The innermost loops of every decode variant must be
-    # free of scratch accesses.
+    # prefetch pipeline.  Every block of the tile loops (loop depth 2 and
+    # deeper: inside the loop over work units) must be free of scratch
+    # accesses.
     sym = f"_ZN3mla13decode_kernel{variant}EEvNS_10DecodeArgsE:"
     start = compiled.index(sym)
     body = compiled[start:compiled.index(".Lfunc_end", start)].splitlines()
-    headers = [i for i, l in enumerate(body) if "Inner Loop Header" in l]
-    assert headers, "no inner loop found"
-    for h in headers:
-        label = body[h - 1].split(":")[0]
-        ends = [i for i, l in enumerate(body) if label in l and "branch" in l and i > h]
-        seg = body[h:max(ends) + 1]
-        assert not any("scratch_" in l for l in seg), f"spill in loop {label}"
+    blocks = _blocks_with_depth(body)
+    deep = [b["lines"] for b in blocks if b["depth"] >= 2]
+    assert deep, "no tile loop found"
+    for lines in deep:
+        assert not any("scratch_" in l for l in lines), f"spill in loop block {lines[0].split()[0]}"
+
+
+def test_block_depths_parsed():
+    body = [".LBB0_1:  ; %bb.0", "\tv_mov_b32 v0, 0", ".LBB0_2:  ; Parent Loop BB0_1 Depth=1",
+            "  ; =>  This Inner Loop Header: Depth=2", "\tscratch_load_dword v1, off, s0",
+            "; %bb.3:  ; in Loop: Header=BB0_2 Depth=2", "\ts_nop 0", ".LBB0_4:",
+            "\ts_endpgm"]
+    got = [(b["lines"][0].split(":")[0], b["depth"]) for b in _blocks_with_depth(body)]
+    assert got == [(".LBB0_1", 0), (".LBB0_2", 2), ("; %bb.3", 2), (".LBB0_4", 0)]
