@@ -31,6 +31,21 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode us/layer + achieved KV HBM TB/s (% of peak) at 100k ctx, q_len 5"
 HBM_PEAK_TBPS = 8.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 (e4m3) MFMA, vendor figure
+
+
+def mfma_peak_tflops(kv_dtype: str) -> float:
+    """MFMA peak that prices the decode kernel's algorithmic FLOPs.
+
+    Each contraction takes the peak of the type it runs in.  BF16 KV: both
+    products on bf16 MFMAs.  FP8 KV: the c_kv parts of Q.K and P.V (2 * 512
+    + 2 * 512 of the 2176 FLOP per row and token) run on e4m3 MFMAs, the
+    RoPE part (2 * 64) on bf16 MFMAs, so the floor is the sum of the two
+    times and the effective peak 2176 / (2048 / 5000 + 128 / 2500).
+    """
+    if kv_dtype == "bf16":
+        return MFMA_BF16_PEAK_TFLOPS
+    return 2176.0 / (2048.0 / MFMA_FP8_PEAK_TFLOPS + 128.0 / MFMA_BF16_PEAK_TFLOPS)
 B200_CONTEXT_US = {"mtp": 1240.0, "dcp8": 826.0}  # the pages' numbers (other hardware)
 
 WORKLOADS = {
@@ -175,7 +190,7 @@ def time_decode(x, dev, steps: int, warmup: int) -> float:
 def run_sweep(args, dev):
     """Batch sweep at 200k tokens, q_len 5, 96 heads, FP8: e(B) = t_floor(B) / t(B).
 
-    t_floor is the bf16-MFMA time of the algorithmic FLOPs at the vendor peak;
+    t_floor is the MFMA time of the algorithmic FLOPs at the vendor peaks;
     no cliff means e(B) varies little over B = 1..24 and t(B) never drops as
     B grows.
     """
@@ -188,7 +203,7 @@ def run_sweep(args, dev):
         torch.cuda.synchronize()
         t_us = time_decode(x, dev, args.steps, args.warmup)
         flops, kv_bytes, _ = algorithmic_counts(x)
-        t_floor = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6
+        t_floor = flops / (mfma_peak_tflops(x.kv_dtype) * 1e12) * 1e6
         rows.append({"batch": B, "tokens": int(np.sum(x.seq_lens)), "us_per_layer": round(t_us, 1),
                      "kv_tb_per_s": round(kv_bytes / (t_us * 1e-6) / 1e12, 3),
                      "e": round(t_floor / t_us, 4)})
@@ -382,9 +397,10 @@ def main():
     # average duration; the merge of split requests is not in it.
     k_tflops = flops / (k_us * 1e-6) / 1e12
     traffic = committed_traffic(args.workload)
+    peak = mfma_peak_tflops(x.kv_dtype)
     roofline = {
-        "bound": "mfma", "achieved": round(k_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "bound": "mfma", "achieved": round(k_tflops, 2), "peak": round(peak, 1),
+        "unit": "TFLOP/s", "frac": round(k_tflops / peak, 4),
         "traffic": traffic, "kernel": "mla::decode_kernel", "kernel_us": round(k_us, 2),
         "flops_per_launch": flops, "algorithmic_bytes_per_launch": all_bytes,
     }
@@ -406,14 +422,14 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if x.kv_dtype == "bf16" else "fp8_e4m3+bf16",
         "data": "synthetic",
         "config": {"workload": CONFIGS[cfg]["name"], "requests": x.batch,
                    "context": int(max(x.seq_lens)), "q_len": x.q_len, "heads": x.num_heads,
                    "kv": x.kv_dtype, "page_size": x.page_size, "dcp": [x.dcp_size, x.dcp_rank]},
         "kv_tb_per_s": round(kv_tbps, 3),
         "kv_hbm_peak_frac": round(kv_tbps / HBM_PEAK_TBPS, 4),
-        "mfma_bf16_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "mfma_frac": round(tflops / peak, 4),
         "step_us_p10_p50_p90": [round(float(np.percentile(times_ms, p)) * 1e3, 2)
                                 for p in (10, 50, 90)],
         "merge_us": round(t_us - k_us, 2),
