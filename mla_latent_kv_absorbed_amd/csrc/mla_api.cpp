@@ -10,9 +10,10 @@
 // length) for each of its G = ceil(q_len H / 128) row groups, plus a fixed
 // per-unit overhead (loading Q, writing O).  The concatenated work of all
 // requests is cut into S equal pieces (S = compute units / G); piece s runs on
-// G workgroups, one per row group, that stream the same tokens.  Those G
-// siblings get workgroup ids congruent modulo 8, so that with round-robin
-// dispatch over the 8 XCDs they share one XCD and its L2.  A request cut by
+// G workgroups, one per row group, that stream the same tokens.  Workgroups
+// are dispatched round-robin over the 8 XCDs (id modulo 8), each with its own
+// L2: the G siblings get ids of one XCD, and each XCD takes a contiguous run
+// of pieces, so that the pieces of a request mostly share one L2.  A request cut by
 // piece boundaries produces one partial (O, LSE) per piece, merged by LSE
 // afterwards (same page: partial results are merged by log-sum-exp).
 
@@ -242,14 +243,28 @@ mla_status mla_decode_plan(const mla_decode_desc* d, const int32_t* seq_lens_hos
     num_wgs = S * G;
     for (int64_t s = 0; s < S; ++s)
       for (int g = 0; g < G; ++g) wg_of[s * G + g] = s * G + g;
-  } else {
+  } else if (8 * G * ((S + 7) / 8) <= cus) {
+    // XCD k (workgroup ids congruent to k modulo 8) takes a contiguous run
+    // of pieces, so that the pieces of one request share its L2 (and load
+    // its Q rows once), and the G siblings of a piece take ids of the same
+    // XCD (they stream the same KV tiles).  The first S % 8 XCDs take one
+    // piece more; the ids this leaves unused are the highest ones, and all
+    // ids stay below the number of compute units.
+    const int64_t q = S / 8, r = S % 8;
     num_wgs = 0;
-    for (int64_t s = 0; s < S; ++s)
+    for (int64_t s = 0; s < S; ++s) {
+      const int64_t k = s < r * (q + 1) ? s / (q + 1) : r + (s - r * (q + 1)) / q;
+      const int64_t slot = s < r * (q + 1) ? s % (q + 1) : (s - r * (q + 1)) % q;
       for (int g = 0; g < G; ++g) {
-        const int64_t x = (s % 8) + 8 * (G * (s / 8) + g);
+        const int64_t x = k + 8 * (G * slot + g);
         wg_of[s * G + g] = x;
         num_wgs = std::max(num_wgs, x + 1);
       }
+    }
+  } else {
+    num_wgs = S * G;
+    for (int64_t s = 0; s < S; ++s)
+      for (int g = 0; g < G; ++g) wg_of[s * G + g] = s * G + g;
   }
   std::vector<std::vector<Unit>> per_wg(num_wgs);
   std::vector<int> next_part(B, 0);

@@ -98,6 +98,35 @@ def test_siblings_share_an_xcd_and_grid_fits_the_chip():
         assert len(xs) == 4 and len({x % 8 for x in xs}) == 1, key
 
 
+def _owners(p):
+    wgb, u = p.wg_begin(), p.units()
+    return [(x, u[k]) for x in range(len(wgb) - 1) for k in range(wgb[x], wgb[x + 1])]
+
+
+def test_pieces_of_a_request_share_an_xcd():
+    # 32 requests cut into 8 pieces each on 256 CUs: the 8 pieces of a request
+    # run on one XCD (ids congruent modulo 8), which then loads its Q once.
+    p = mla.make_plan(mla.make_desc(32, 1, 128, "bf16", num_cus=256), [4096] * 32)
+    assert p.header["num_wgs"] == 256
+    xcds = {}
+    for x, unit in _owners(p):
+        xcds.setdefault(int(unit[0]), set()).add(x % 8)
+    assert all(len(v) == 1 for v in xcds.values())
+    assert sorted(len([b for b in xcds if xcds[b] == {k}]) for k in range(8)) == [4] * 8
+
+
+def test_grid_never_exceeds_the_compute_units():
+    rng = np.random.default_rng(11)
+    for _ in range(60):
+        B = int(rng.integers(1, 40))
+        q = int(rng.integers(1, 9))
+        H = int(rng.choice([16, 32, 96, 128]))
+        lens = rng.integers(q, 300000, size=B)
+        cus = int(rng.choice([8, 100, 120, 256, 304]))
+        p = mla.make_plan(mla.make_desc(B, q, H, "fp8", num_cus=cus), lens)
+        assert p.header["num_wgs"] <= cus
+
+
 @pytest.mark.parametrize("lens", [[100000] * 16, [4096] * 32, [200000] * 24,
                                   list(ragged_lengths(5, 64, 1024, 400000))])
 def test_plan_is_balanced(lens):
