@@ -344,7 +344,9 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--flush-mb", type=int, default=0,
-                    help="write this many MB between steps (outside the events) to evict L2/MALL")
+                    help="read this many MB between steps (outside the events) to evict L2/MALL; "
+                         "a read leaves the caches holding clean lines, so the timed kernel pays "
+                         "no write-back for the eviction")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the one-line step benchmark: time the batch sweep at "
                          "200k tokens (B in 1..24, and the ragged 64-request batch) and "
@@ -386,7 +388,8 @@ def main():
     out = torch.empty((x.batch, x.q_len, x.num_heads, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((x.batch, x.q_len, x.num_heads), dtype=torch.float32, device=dev)
     ws = torch.zeros(max(h["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
-    flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev) if args.flush_mb else None
+    flush = (torch.ones(args.flush_mb << 18, dtype=torch.int32, device=dev)
+             if args.flush_mb else None)
     stream = torch.cuda.current_stream(dev)
 
     def step(mid=None):
@@ -419,14 +422,14 @@ def main():
 
     def flushed_step():
         if flush is not None:
-            flush.zero_()
+            flush.sum()
         step()
 
     queue_ahead(flushed_step, args.steps, args.warmup)
     t0 = time.perf_counter()
     for k in range(args.steps):
         if flush is not None:
-            flush.zero_()
+            flush.sum()
         starts[k].record(stream)
         step(mids[k])
         ends[k].record(stream)
