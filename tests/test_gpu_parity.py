@@ -29,10 +29,11 @@ def oracle(x, reqs=None, **kw):
                           x.kv_dtype, x.dcp_size, x.dcp_rank, **kw)
 
 
-def gpu_decode(x, force_splits=0, page_size=None, plan_out=None):
+def gpu_decode(x, force_splits=0, page_size=None, plan_out=None, num_cus=0):
     ps = x.page_size if page_size is None else page_size
     desc = mla.make_desc(x.batch, x.q_len, x.num_heads, x.kv_dtype, page_size=ps,
-                         dcp_size=x.dcp_size, dcp_rank=x.dcp_rank, force_splits=force_splits)
+                         dcp_size=x.dcp_size, dcp_rank=x.dcp_rank, force_splits=force_splits,
+                         num_cus=num_cus)
     plan = mla.make_plan(desc, x.seq_lens, device=DEV)
     if plan_out is not None:
         plan_out.append(plan)
@@ -77,6 +78,20 @@ def test_small_shapes(kv, q, H):
     x = make_inputs(40 + q, lens, q, H, kv, kv_std=0.1 if kv == "bf16" else 1.0)
     out, lse = gpu_decode(x)
     check(out, lse, *oracle(x), tag=f"{kv} q{q} h{H} lens {lens}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("q,H,splits", [(1, 8, 5), (5, 96, 9), (2, 112, 3), (5, 96, 0)])
+def test_rows_past_the_request_end(kv, q, H, splits):
+    # Row groups whose last waves hold no valid row (8 rows: waves 1-3 of
+    # the group are empty; 480 rows: wave 3 of group 3; 224 rows: wave 3 of
+    # group 1), with units of a single tile (32-token cuts of short
+    # requests) and a 1-token request.  splits 0 plans for 8 compute units,
+    # so that each workgroup runs several units in a row.
+    lens = [q, 40, 95, 64 * 3 + 1, 900]
+    x = make_inputs(60 + q, lens, q, H, kv, kv_std=0.1 if kv == "bf16" else 1.0)
+    out, lse = gpu_decode(x, force_splits=splits, num_cus=8 if splits == 0 else 0)
+    check(out, lse, *oracle(x), tag=f"{kv} q{q} h{H} splits {splits} lens {lens}")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
