@@ -27,6 +27,9 @@ Sources (all on the page "Kimi K3 decode: DP16 vs DP2 x DCP8" and the page
 
 The formula itself is never written on the pages; the readings taken where
 they are silent are listed in the module docstring of ``mla_ref``.
+
+``prepare_ref`` is the oracle of the step before attention (Q absorption,
+RoPE, KV append); its readings are in its own module docstring.
 """
 
 from .mla_ref import (  # noqa: F401
@@ -46,4 +49,16 @@ from .mla_ref import (  # noqa: F401
     softmax_reduce,
     mla_decode_ref,
     lse_combine_ref,
+)
+from .prepare_ref import (  # noqa: F401
+    e4m3fn_encode,
+    f32_to_bf16_bits,
+    bf16_bits_to_f32,
+    rope_f32,
+    q_absorb_ref,
+    q_rope_ref,
+    latent_rows_ref,
+    fp8_quantise_rows,
+    kv_append_ref,
+    mla_prepare_ref,
 )
