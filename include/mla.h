@@ -175,6 +175,66 @@ mla_status mla_decode_merge(const void* plan_host, const void* plan_device,
 mla_status mla_lse_combine(const float* part_o, const float* part_lse, int32_t num_parts,
                            int64_t rows, float* out, float* lse, void* stream);
 
+/*
+ * MLA prepare: the step before mla_decode, on the T = B * q_len new tokens of
+ * a decode step (page "Kimi K3 decode: DP16 vs DP2 x DCP8": kv_b_proj is
+ * absorbed into w_kc / w_vc, whose w_kc is 96 x 128 x 512 bf16; the step is
+ * the mla_prepare of section "MLA").  It computes:
+ *
+ *   q_nope_absorbed[t, h, n] = sum_k q_nope[t, h, k] * w_kc[h, k, n]
+ *       (fp32 accumulation, rounded to bf16: the decode kernel's query input);
+ *   q_rope_out[t, h, :] = RoPE(q_rope_in[t, h, :], positions[t]);
+ *   pool row slots[t] = [c_kv_new[t] | RoPE(k_rope_new[t], positions[t])],
+ *       as bf16, or for FP8 pools as e4m3fn codes of x / scale with
+ *       scale = amax / 448 over the row's 576 values (1 if all are zero),
+ *       stored in kv_scale[slots[t]].
+ *
+ * RoPE rotates the interleaved pairs (x[2i], x[2i+1]) of a 64-wide vector:
+ * (x0 c - x1 s, x0 s + x1 c) with c = cos_sin[pos, i], s = cos_sin[pos, 32 + i];
+ * products and sums are correctly rounded float32 operations, and the result
+ * is rounded to bf16 (to nearest even) before it is stored or quantised.  The
+ * FP8 scale and the quotients x / scale are correctly rounded float32
+ * divisions, the quotients clamped to [-448, 448] and rounded to the nearest
+ * e4m3fn value (ties to even).
+ *
+ *   num_tokens:      T >= 0 (0: nothing is enqueued).
+ *   num_heads:       H >= 1.
+ *   kv_dtype:        mla_kv_dtype of the pool.
+ *   q_nope:          bf16 [T, H, 128] device, the no-RoPE query parts.
+ *   q_rope_in:       bf16 [T, H, 64] device, the RoPE query parts before rotation.
+ *   w_kc_t:          bf16 [H, 512, 128] device: every head's w_kc transposed,
+ *                    element (h, n, k) = w_kc[h, k, n] (laid out once when the
+ *                    weights are loaded, so that both MFMA operands read rows
+ *                    with k contiguous).
+ *   c_kv_new:        bf16 [T, 512] device, the new tokens' latent.
+ *   k_rope_new:      bf16 [T, 64] device, their RoPE key parts before rotation.
+ *   positions:       int32 [T] device, each token's position (row of cos_sin);
+ *                    values outside [0, max_pos) are clamped into it.
+ *   cos_sin:         fp32 [max_pos, 64] device: cos of the 32 frequencies, then
+ *                    their sin, for every position (the caller's choice of base
+ *                    and scaling).
+ *   slots:           int32 [T] device, the pool slot of each new token's row;
+ *                    a slot outside [0, num_slots) is not stored (for example
+ *                    a token that another DCP shard holds).  Slots must be
+ *                    distinct.
+ *   q_nope_absorbed: bf16 [T, H, 512] device output.
+ *   q_rope_out:      bf16 [T, H, 64] device output (must not alias q_rope_in).
+ *   kv_pool:         [num_slots, 576] device pool (as for mla_decode), written
+ *                    at the stored slots only.
+ *   kv_scale:        fp32 [num_slots] device for FP8 pools (written at the
+ *                    stored slots), NULL for BF16.
+ *   stream:          HIP stream, 0 = default stream.
+ *
+ * All pointers 16-byte aligned (kv_scale 4-byte).  Errors are detected on the
+ * host and returned before anything is enqueued.
+ */
+mla_status mla_prepare(int32_t num_tokens, int32_t num_heads, int32_t kv_dtype,
+                       const void* q_nope, const void* q_rope_in, const void* w_kc_t,
+                       const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
+                       const float* cos_sin, int32_t max_pos, const int32_t* slots,
+                       void* q_nope_absorbed, void* q_rope_out, void* kv_pool, float* kv_scale,
+                       int64_t num_slots, void* stream);
+
 /* Static description of a status code. */
 const char* mla_status_string(mla_status status);
 

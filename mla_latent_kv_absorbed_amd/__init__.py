@@ -2,7 +2,7 @@
 
 The compute runs in hand-written HIP kernels for gfx950 behind the C ABI of
 include/mla.h (libmla.so, built in this directory); this package only
-marshals arguments.  See `decode`, `make_plan`, `lse_combine`.
+marshals arguments.  See `decode`, `make_plan`, `lse_combine`, `prepare`.
 """
 
 from ._binding import (  # noqa: F401
@@ -18,5 +18,6 @@ from ._binding import (  # noqa: F401
     make_desc,
     make_plan,
     plan_max_bytes,
+    prepare,
     status_string,
 )

@@ -66,6 +66,9 @@ def load_library():
     lib.mla_decode_merge.restype = i32
     lib.mla_lse_combine.argtypes = [vp, vp, i32, i64, vp, vp, vp]
     lib.mla_lse_combine.restype = i32
+    lib.mla_prepare.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                vp, i64, vp]
+    lib.mla_prepare.restype = i32
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
     _LIB = lib
@@ -254,3 +257,47 @@ def lse_combine(part_o, part_lse, out=None, lse=None, stream=None):
     if st != MLA_OK:
         raise MlaError("mla_lse_combine failed", st)
     return out, lse
+
+
+def prepare(q_nope, q_rope_in, w_kc_t, c_kv_new, k_rope_new, positions, cos_sin, slots,
+            kv_pool, kv_scale=None, q_nope_absorbed=None, q_rope_out=None, stream=None):
+    """mla_prepare on torch device tensors.
+
+    Shapes: q_nope [T, H, 128], q_rope_in [T, H, 64], w_kc_t [H, 512, 128],
+    c_kv_new [T, 512], k_rope_new [T, 64] (bf16); positions, slots int32 [T];
+    cos_sin fp32 [max_pos, 64]; kv_pool [num_slots, 576] (bf16, or uint8 /
+    float8_e4m3fn with an fp32 kv_scale [num_slots]).  Returns
+    (q_nope_absorbed [T, H, 512], q_rope_out [T, H, 64]); the pool rows at
+    `slots` (and their scales) are written in place.
+    """
+    import torch
+    T, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    dev = q_nope.device
+    bf = torch.bfloat16
+    checks = (("q_nope", q_nope, (T, H, 128), bf), ("q_rope_in", q_rope_in, (T, H, 64), bf),
+              ("w_kc_t", w_kc_t, (H, 512, 128), bf), ("c_kv_new", c_kv_new, (T, 512), bf),
+              ("k_rope_new", k_rope_new, (T, 64), bf), ("positions", positions, (T,), torch.int32),
+              ("slots", slots, (T,), torch.int32))
+    for name, t, shape, dt in checks:
+        if tuple(t.shape) != shape or t.dtype != dt or t.device != dev or not t.is_contiguous():
+            raise MlaError(f"{name} must be a contiguous {dt} tensor of shape {shape} on {dev}")
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != 64 or \
+            not cos_sin.is_contiguous():
+        raise MlaError("cos_sin must be a contiguous float32 [max_pos, 64] tensor")
+    fp8 = kv_pool.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != 576 or not (fp8 or kv_pool.dtype == bf):
+        raise MlaError("kv_pool must be [num_slots, 576] of bf16 or e4m3fn bytes")
+    if fp8 and (kv_scale is None or kv_scale.dtype != torch.float32):
+        raise MlaError("FP8 pools need an fp32 kv_scale per slot")
+    if q_nope_absorbed is None:
+        q_nope_absorbed = torch.empty((T, H, 512), dtype=bf, device=dev)
+    if q_rope_out is None:
+        q_rope_out = torch.empty((T, H, 64), dtype=bf, device=dev)
+    st = load_library().mla_prepare(
+        T, H, KV_FP8 if fp8 else KV_BF16, _ptr(q_nope), _ptr(q_rope_in), _ptr(w_kc_t),
+        _ptr(c_kv_new), _ptr(k_rope_new), _ptr(positions), _ptr(cos_sin), int(cos_sin.shape[0]),
+        _ptr(slots), _ptr(q_nope_absorbed), _ptr(q_rope_out), _ptr(kv_pool),
+        _ptr(kv_scale if fp8 else None), int(kv_pool.shape[0]), _stream(stream))
+    if st != MLA_OK:
+        raise MlaError("mla_prepare failed", st)
+    return q_nope_absorbed, q_rope_out

@@ -106,6 +106,44 @@ void plan_bounds(const mla_decode_desc* d, int cus, int64_t* max_wgs, int64_t* m
 
 extern "C" {
 
+mla_status mla_prepare(int32_t num_tokens, int32_t num_heads, int32_t kv_dtype,
+                       const void* q_nope, const void* q_rope_in, const void* w_kc_t,
+                       const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
+                       const float* cos_sin, int32_t max_pos, const int32_t* slots,
+                       void* q_nope_absorbed, void* q_rope_out, void* kv_pool, float* kv_scale,
+                       int64_t num_slots, void* stream) {
+  if (num_tokens < 0 || num_heads < 1 || max_pos < 1 || num_slots < 1) return MLA_ERR_INVALID_ARG;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARG;
+  const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
+  for (const void* p : {q_nope, q_rope_in, w_kc_t, c_kv_new, k_rope_new, (const void*)positions,
+                        (const void*)cos_sin, (const void*)slots, (const void*)q_nope_absorbed,
+                        (const void*)q_rope_out, (const void*)kv_pool})
+    if (!p || !aligned16(p)) return MLA_ERR_INVALID_ARG;
+  if (fp8 && (!kv_scale || (reinterpret_cast<uintptr_t>(kv_scale) & 3u))) return MLA_ERR_INVALID_ARG;
+  if (q_rope_out == q_rope_in) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)num_tokens * num_heads > INT32_MAX / 64) return MLA_ERR_INVALID_ARG;
+  PrepareArgs a{};
+  a.T = num_tokens;
+  a.H = num_heads;
+  a.max_pos = max_pos;
+  a.fp8 = fp8;
+  a.num_slots = num_slots;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_rope_in = static_cast<const uint16_t*>(q_rope_in);
+  a.w_kc_t = static_cast<const uint16_t*>(w_kc_t);
+  a.c_kv_new = static_cast<const uint16_t*>(c_kv_new);
+  a.k_rope_new = static_cast<const uint16_t*>(k_rope_new);
+  a.positions = positions;
+  a.cos_sin = cos_sin;
+  a.slots = slots;
+  a.q_nope_absorbed = static_cast<uint16_t*>(q_nope_absorbed);
+  a.q_rope_out = static_cast<uint16_t*>(q_rope_out);
+  a.pool = kv_pool;
+  a.kv_scale = fp8 ? kv_scale : nullptr;
+  if (launch_prepare(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_status_string(mla_status s) {
   switch (s) {
     case MLA_OK: return "ok";

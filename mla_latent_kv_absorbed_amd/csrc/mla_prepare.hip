@@ -1,0 +1,163 @@
+// MLA prepare: the step before absorbed decode, on the T new query tokens of
+// a decode step (page "Kimi K3 decode: DP16 vs DP2 x DCP8": kv_b_proj is
+// absorbed into w_kc / w_vc, w_kc is 96 x 128 x 512 in bf16, and the step is
+// the mla_prepare of section "MLA").
+//
+// q_absorb_kernel   q_nope_absorbed[t, h, :] = q_nope[t, h, :] . w_kc[h]
+//                   (128 -> 512 per head) on bf16 MFMAs, fp32 accumulation,
+//                   rounded to bf16.  HBM-bound: every head's 128 KB of
+//                   weights is read once.
+// rope_append_kernel  RoPE of every head's q_rope and of the new tokens'
+//                   k_rope (interleaved pairs, caller-given cos / sin), then
+//                   the append of the rows [c_kv | roped k_rope] to the pool
+//                   at the given slots: BF16 bits, or e4m3fn codes with the
+//                   per-token scale amax / 448.
+//
+// Every float32 step that decides a stored bit (the roped values, the scale,
+// the quotients) is a correctly rounded IEEE operation with no contraction,
+// so that the stored bytes are reproducible on the host.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) {
+  return __builtin_bit_cast(float, u & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return bf16_bits(a) | (bf16_bits(b) << 16);
+}
+
+// One interleaved RoPE pair (x0, x1) -> (x0 c - x1 s, x0 s + x1 c), every
+// product and sum rounded on its own (no fused multiply-add).
+__device__ __forceinline__ uint32_t rope_pair(uint32_t xx, float c, float s) {
+#pragma clang fp contract(off)
+  const float x0 = bf16_lo(xx), x1 = bf16_hi(xx);
+  const float y0 = x0 * c - x1 * s;
+  const float y1 = x0 * s + x1 * c;
+  return pack_bf16(y0, y1);
+}
+
+// Block (head h, column quarter qb): wave w computes the 32 columns
+// n0 = 128 qb + 32 w .. + 32 for every token, 32 tokens per MFMA block.
+// v_mfma_f32_32x32x16_bf16: lane l holds A[row l % 32][k 8 (l / 32) .. + 8]
+// (a token's q_nope) and B[k 8 (l / 32) .. + 8][column l % 32] (a row of
+// w_kc_t, k contiguous); accumulator r holds D[row 8 (r / 4) + 4 (l / 32) +
+// r % 4][column l % 32].
+__global__ __launch_bounds__(256) void q_absorb_kernel(const uint16_t* q_nope,
+                                                       const uint16_t* w_kc_t, uint16_t* out,
+                                                       int T, int H) {
+  const int h = blockIdx.x >> 2, qb = blockIdx.x & 3;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 31, kh = lane >> 5;
+  const int n0 = 128 * qb + 32 * w;
+  const bf16x8* wrow =
+      reinterpret_cast<const bf16x8*>(w_kc_t + ((int64_t)h * 512 + n0 + j) * 128 + 8 * kh);
+  bf16x8 bop[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) bop[ks] = wrow[2 * ks];
+  for (int t0 = 0; t0 < T; t0 += 32) {
+    const int t = t0 + j;
+    bf16x8 aop[8];
+    if (t < T) {
+      const bf16x8* qrow =
+          reinterpret_cast<const bf16x8*>(q_nope + ((int64_t)t * H + h) * 128 + 8 * kh);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) aop[ks] = qrow[2 * ks];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) aop[ks] = bf16x8{};
+    }
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[ks], bop[ks], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ti = t0 + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (ti < T) out[((int64_t)ti * H + h) * 512 + n0 + j] = (uint16_t)bf16_bits(acc[r]);
+    }
+  }
+}
+
+__device__ __forceinline__ float block_max_256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// e4m3fn code of a float32 already inside [-448, 448], nearest-even.
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+// One block per new token.  Threads 0..255 rotate the token's q_rope pairs
+// (H x 32 of them), then thread i takes c_kv elements 2 i, 2 i + 1 and
+// threads 0..31 the k_rope pair i of the row to append.
+__global__ __launch_bounds__(256) void rope_append_kernel(PrepareArgs a) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  int pos = a.positions[t];
+  pos = pos < 0 ? 0 : (pos >= a.max_pos ? a.max_pos - 1 : pos);
+  const float* cs = a.cos_sin + (int64_t)pos * 64;
+
+  const uint32_t* qin = reinterpret_cast<const uint32_t*>(a.q_rope_in + (int64_t)t * a.H * 64);
+  uint32_t* qout = reinterpret_cast<uint32_t*>(a.q_rope_out + (int64_t)t * a.H * 64);
+  for (int p = tid; p < a.H * 32; p += 256) {
+    const int i = p & 31;
+    qout[p] = rope_pair(qin[p], cs[i], cs[32 + i]);
+  }
+
+  const int64_t slot = a.slots[t];
+  if (slot < 0 || slot >= a.num_slots) return;  // uniform in the block
+  const uint32_t ckv = reinterpret_cast<const uint32_t*>(a.c_kv_new + (int64_t)t * 512)[tid];
+  uint32_t kr = 0;
+  if (tid < 32) {
+    const uint32_t kin = reinterpret_cast<const uint32_t*>(a.k_rope_new + (int64_t)t * 64)[tid];
+    kr = rope_pair(kin, cs[tid], cs[32 + tid]);
+  }
+  if (!a.fp8) {
+    uint32_t* row = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.pool) + slot * 576);
+    row[tid] = ckv;
+    if (tid < 32) row[256 + tid] = kr;
+    return;
+  }
+  const float c0 = bf16_lo(ckv), c1 = bf16_hi(ckv);
+  const float r0 = bf16_lo(kr), r1 = bf16_hi(kr);
+  float m = fmaxf(fabsf(c0), fabsf(c1));
+  if (tid < 32) m = fmaxf(m, fmaxf(fabsf(r0), fabsf(r1)));
+  const float amax = block_max_256(m, red);
+  const float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  auto quot = [&](float x) { return fminf(fmaxf(__fdiv_rn(x, scale), -448.0f), 448.0f); };
+  uint16_t* row = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.pool) + slot * 576);
+  row[tid] = (uint16_t)e4m3_pair(quot(c0), quot(c1));
+  if (tid < 32) row[256 + tid] = (uint16_t)e4m3_pair(quot(r0), quot(r1));
+  if (tid == 0) a.kv_scale[slot] = scale;
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const PrepareArgs& args, hipStream_t stream) {
+  if (args.T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(q_absorb_kernel, dim3((unsigned)args.H * 4), dim3(256), 0, stream,
+                     args.q_nope, args.w_kc_t, args.q_nope_absorbed, args.T, args.H);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rope_append_kernel, dim3((unsigned)args.T), dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -159,13 +159,14 @@ def kv_append_ref(pool, kv_scale, c_kv_bits, k_rope_bits, cos_sin, positions, sl
     """Pool (and scales) after appending the T new rows at `slots`.
 
     pool: uint16 BF16 bits [num_slots, 576] or uint8 e4m3fn codes; kv_scale:
-    float32 [num_slots] (FP8) or None.  Slots < 0 are skipped; the others
-    must be distinct.  Returns new arrays; the inputs are not modified.
+    float32 [num_slots] (FP8) or None.  Slots outside [0, num_slots) are
+    skipped (a token another DCP shard holds); the others must be distinct.
+    Returns new arrays; the inputs are not modified.
     """
     rows = latent_rows_ref(c_kv_bits, k_rope_bits, cos_sin, positions)
     sl = np.asarray(slots, dtype=np.int64)
-    keep = sl >= 0
     pool = np.array(pool, copy=True)
+    keep = (sl >= 0) & (sl < pool.shape[0])
     if kv_dtype == "bf16":
         pool[sl[keep]] = rows[keep]
         return pool, None

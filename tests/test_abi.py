@@ -148,3 +148,27 @@ def test_plan_header_fields():
     assert h["rows"] == 480 and h["row_groups"] == 4
     assert h["max_local"] == 12500 and h["dcp_size"] == 8 and h["dcp_rank"] == 5
     assert h["plan_bytes"] == len(p.host) and h["page_size"] == 64
+
+
+def test_prepare_rejects_bad_arguments_on_host():
+    lib = mla.load_library()
+    f = 1 << 20  # never dereferenced: validation fails first (or T = 0 enqueues nothing)
+    g = f + 4096
+
+    def call(T=4, H=2, kv=1, ptrs=None, max_pos=8, nslots=16, scale=f):
+        p = ptrs or [f] * 5
+        return lib.mla_prepare(T, H, kv, p[0], p[1], p[2], p[3], p[4], f, f, max_pos, f, f, g,
+                               f, scale, nslots, None)
+    assert call(T=0) == 0
+    assert call(T=0, kv=0, scale=None) == 0
+    assert call(T=-1) == -1
+    assert call(H=0) == -1
+    assert call(kv=2) == -1
+    assert call(max_pos=0) == -1
+    assert call(nslots=0) == -1
+    assert call(ptrs=[None, f, f, f, f]) == -1
+    assert call(ptrs=[f, f, f + 8, f, f]) == -1     # misaligned w_kc_t
+    assert call(scale=None) == -1                    # FP8 pool without scales
+    assert call(scale=f + 2) == -1                   # misaligned scales
+    # q_rope_out aliasing q_rope_in
+    assert lib.mla_prepare(4, 2, 0, f, g, f, f, f, f, f, 8, f, f, g, f, None, 16, None) == -1
