@@ -118,6 +118,84 @@ def algorithmic_counts(x):
     return flops, kv_bytes, kv_bytes + other
 
 
+def prepare_bytes(x) -> float:
+    """Algorithmic HBM bytes of one mla_prepare call: w_kc read once, the
+    queries read and written once, the new rows and their positions' cos /
+    sin read once, and the pool rows (and FP8 scales) written once."""
+    T, H = x["T"], x["H"]
+    e = 1 if x["kv_dtype"] == "fp8" else 2
+    return float(H * 512 * 128 * 2 + T * H * 128 * 2 + 2 * T * H * 64 * 2 + T * H * 512 * 2
+                 + T * 576 * 2 + T * 64 * 4 + T * (576 * e + (4 if e == 1 else 0)) + T * 8)
+
+
+def run_prepare(args, dev):
+    """mla_prepare (Q absorption, RoPE, KV append) on the prepare workloads.
+
+    Per workload: mean event-timed us per call (both kernels), algorithmic
+    HBM bytes / time against 8 TB/s, and the CPU oracle on the same inputs.
+    """
+    import torch
+    import mla_latent_kv_absorbed_amd as mla
+    from oracle import mla_prepare_ref
+    from workload import PREPARE_CONFIGS, prepare_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    rows = []
+    stream = torch.cuda.current_stream(dev)
+    for key in PREPARE_CONFIGS:
+        x = prepare_inputs(key, device=dev)
+        qa = torch.empty((x["T"], x["H"], 512), dtype=torch.bfloat16, device=dev)
+        qr = torch.empty((x["T"], x["H"], 64), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            mla.prepare(x["q_nope"], x["q_rope_in"], x["w_kc_t"], x["c_kv_new"], x["k_rope_new"],
+                        x["positions"], x["cos_sin"], x["slots"], x["kv_pool"], x["kv_scale"],
+                        q_nope_absorbed=qa, q_rope_out=qr, stream=stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        queue_ahead(step, args.steps, args.warmup)
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev]) * 1e3)
+        nbytes = prepare_bytes(x)
+        # The oracle on the same inputs (host copies), timed once.
+        bits = {k: x[k].cpu().view(torch.int16).numpy().view(np.uint16)
+                for k in ("q_nope", "q_rope_in", "w_kc_t", "c_kv_new", "k_rope_new")}
+        pool = x["kv_pool"].cpu()
+        pool = pool.view(torch.int16).numpy().view(np.uint16) if x["kv_dtype"] == "bf16" \
+            else pool.numpy()
+        sc = None if x["kv_scale"] is None else x["kv_scale"].cpu().numpy()
+        t0 = time.perf_counter()
+        mla_prepare_ref(bits["q_nope"], bits["q_rope_in"], bits["w_kc_t"], bits["c_kv_new"],
+                        bits["k_rope_new"], x["cos_sin"].cpu().numpy(),
+                        x["positions"].cpu().numpy(), x["slots"].cpu().numpy(), pool, sc,
+                        x["kv_dtype"])
+        cpu_us = (time.perf_counter() - t0) * 1e6
+        rows.append({"workload": x["name"], "tokens": x["T"], "heads": x["H"],
+                     "kv": x["kv_dtype"], "us_per_call": round(us, 2),
+                     "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                  "peak": HBM_PEAK_TBPS * 1e3, "unit": "GB/s",
+                                  "frac": round(nbytes / (us * 1e-6) / 1e12 / HBM_PEAK_TBPS, 4),
+                                  "algorithmic_bytes": nbytes},
+                     "cpu_baseline": {"value": round(cpu_us, 1), "unit": "us/call",
+                                      "cores": int(cores), "kind": "oracle",
+                                      "sample": "one call on the same inputs (float64 absorption, "
+                                                "float32 RoPE and quantisation in numpy)"}})
+        log(f"  prepare {x['name']}: {us:.2f} us")
+        del x
+        torch.cuda.empty_cache()
+    print(json.dumps({"prepare": rows, "steps": args.steps, "warmup": args.warmup,
+                      "context_b200": "mla_prepare: 0.44 ms per step in total over the 24 MLA "
+                                      "layers (about 18 us per layer) for 640 rows (DP16-vs-DP2 "
+                                      "page, section MLA)"}), flush=True)
+
+
 def cpu_baseline(x, max_requests: int, budget_s: float):
     """Time the float64 oracle on a bounded sample of requests, scale to the layer."""
     import torch
@@ -355,6 +433,10 @@ def main():
                     help="instead of the one-line step benchmark: run all 8 shards of the DCP "
                          "workload plus mla_lse_combine, and print per-shard, sum and "
                          "combine times as one JSON object")
+    ap.add_argument("--prepare", action="store_true",
+                    help="instead of the one-line step benchmark: time mla_prepare (Q "
+                         "absorption, RoPE, KV append) on the prepare workloads and print one "
+                         "JSON object")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before the warmup, run one plain device copy of this many MB (for "
                          "scaling HBM counters); not timed")
@@ -375,6 +457,9 @@ def main():
         return
     if args.dcp_full:
         run_dcp_full(args, dev)
+        return
+    if args.prepare:
+        run_prepare(args, dev)
         return
     cfg = WORKLOADS[args.workload]
     log(f"generating inputs for {CONFIGS[cfg]['name']} on {dev}")

@@ -3,11 +3,11 @@
 // absorbed into w_kc / w_vc, w_kc is 96 x 128 x 512 in bf16, and the step is
 // the mla_prepare of section "MLA").
 //
-// q_absorb_kernel   q_nope_absorbed[t, h, :] = q_nope[t, h, :] . w_kc[h]
+// Absorption       q_nope_absorbed[t, h, :] = q_nope[t, h, :] . w_kc[h]
 //                   (128 -> 512 per head) on bf16 MFMAs, fp32 accumulation,
 //                   rounded to bf16.  HBM-bound: every head's 128 KB of
 //                   weights is read once.
-// rope_append_kernel  RoPE of every head's q_rope and of the new tokens'
+// RoPE and append  RoPE of every head's q_rope and of the new tokens'
 //                   k_rope (interleaved pairs, caller-given cos / sin), then
 //                   the append of the rows [c_kv | roped k_rope] to the pool
 //                   at the given slots: BF16 bits, or e4m3fn codes with the
@@ -49,43 +49,73 @@ __device__ __forceinline__ uint32_t rope_pair(uint32_t xx, float c, float s) {
   return pack_bf16(y0, y1);
 }
 
-// Block (head h, column quarter qb): wave w computes the 32 columns
-// n0 = 128 qb + 32 w .. + 32 for every token, 32 tokens per MFMA block.
+// Block (head h, column quarter qb, token group): wave w computes columns
+// n0 = 128 qb + 32 w .. + 32, 32 tokens per MFMA block.
 // v_mfma_f32_32x32x16_bf16: lane l holds A[row l % 32][k 8 (l / 32) .. + 8]
 // (a token's q_nope) and B[k 8 (l / 32) .. + 8][column l % 32] (a row of
-// w_kc_t, k contiguous); accumulator r holds D[row 8 (r / 4) + 4 (l / 32) +
-// r % 4][column l % 32].
-__global__ __launch_bounds__(256) void q_absorb_kernel(const uint16_t* q_nope,
-                                                       const uint16_t* w_kc_t, uint16_t* out,
-                                                       int T, int H) {
-  const int h = blockIdx.x >> 2, qb = blockIdx.x & 3;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// w_kc_t, k contiguous, kept in registers); accumulator r holds D[row
+// 8 (r / 4) + 4 (l / 32) + r % 4][column l % 32].
+// The 32 q_nope rows of a block (256 B each) are loaded once per block by
+// all 256 threads with row-contiguous 16-byte loads (issued one block ahead)
+// and shared through LDS; the block's 32 x 128 result goes back through LDS
+// and out as whole 256-byte row segments.
+constexpr int kQStride = 136;   // LDS row stride of a q block, in bf16 (128 + 8 pad)
+constexpr int kOStride = 136;   // LDS row stride of a result tile, in bf16 (128 + 8 pad)
+
+__device__ __forceinline__ void q_absorb_block(const uint16_t* q_nope, const uint16_t* w_kc_t,
+                                               uint16_t* out, int T, int H, int blk, int tb,
+                                               int te, uint16_t* qs, uint16_t* os) {
+  const int h = blk >> 2, qb = blk & 3;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
   const int j = lane & 31, kh = lane >> 5;
   const int n0 = 128 * qb + 32 * w;
-  const bf16x8* wrow =
-      reinterpret_cast<const bf16x8*>(w_kc_t + ((int64_t)h * 512 + n0 + j) * 128 + 8 * kh);
   bf16x8 bop[8];
+  {
+    const bf16x8* wrow =
+        reinterpret_cast<const bf16x8*>(w_kc_t + ((int64_t)h * 512 + n0 + j) * 128 + 8 * kh);
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) bop[ks] = wrow[2 * ks];
-  for (int t0 = 0; t0 < T; t0 += 32) {
-    const int t = t0 + j;
-    bf16x8 aop[8];
-    if (t < T) {
-      const bf16x8* qrow =
-          reinterpret_cast<const bf16x8*>(q_nope + ((int64_t)t * H + h) * 128 + 8 * kh);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) aop[ks] = qrow[2 * ks];
+    for (int ks = 0; ks < 8; ++ks) bop[ks] = wrow[2 * ks];
+  }
+  // Cooperative q load: thread i takes row i / 8, bytes 32 (i % 8) .. + 32.
+  const int lr = tid >> 3, lc = 16 * (tid & 7);  // row, first bf16 column
+  auto gload = [&](int t0, uint4& x0, uint4& x1) {
+    const int t = t0 + lr;
+    if (t < te) {
+      const uint4* src = reinterpret_cast<const uint4*>(q_nope + ((int64_t)t * H + h) * 128 + lc);
+      x0 = src[0];
+      x1 = src[1];
     } else {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) aop[ks] = bf16x8{};
+      x0 = x1 = uint4{0u, 0u, 0u, 0u};
     }
+  };
+  uint4 x0, x1;
+  gload(tb, x0, x1);
+  for (int t0 = tb; t0 < te; t0 += 32) {
+    __syncthreads();  // the previous block's LDS reads are done
+    *reinterpret_cast<uint4*>(qs + lr * kQStride + lc) = x0;
+    *reinterpret_cast<uint4*>(qs + lr * kQStride + lc + 8) = x1;
+    __syncthreads();
+    if (t0 + 32 < te) gload(t0 + 32, x0, x1);
+    bf16x8 aop[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      aop[ks] = *reinterpret_cast<const bf16x8*>(qs + j * kQStride + 16 * ks + 8 * kh);
     f32x16 acc = {};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[ks], bop[ks], acc, 0, 0, 0);
+    for (int ks = 0; ks < 8; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[ks], bop[ks], acc, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int ti = t0 + 8 * (r >> 2) + 4 * kh + (r & 3);
-      if (ti < T) out[((int64_t)ti * H + h) * 512 + n0 + j] = (uint16_t)bf16_bits(acc[r]);
+    for (int r = 0; r < 16; ++r)
+      os[(8 * (r >> 2) + 4 * kh + (r & 3)) * kOStride + 32 * w + j] = (uint16_t)bf16_bits(acc[r]);
+    __syncthreads();
+    // Thread i writes row i / 8, columns 16 (i % 8) .. + 16 of the tile.
+    const int t = t0 + lr;
+    if (t < te) {
+      const uint4* src = reinterpret_cast<const uint4*>(os + lr * kOStride + lc);
+      uint4* dst = reinterpret_cast<uint4*>(out + ((int64_t)t * H + h) * 512 + 128 * qb + lc);
+      dst[0] = src[0];
+      dst[1] = src[1];
     }
   }
 }
@@ -106,28 +136,28 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
 // One block per new token.  Threads 0..255 rotate the token's q_rope pairs
 // (H x 32 of them), then thread i takes c_kv elements 2 i, 2 i + 1 and
 // threads 0..31 the k_rope pair i of the row to append.
-__global__ __launch_bounds__(256) void rope_append_kernel(PrepareArgs a) {
-  __shared__ float red[4];
-  const int t = blockIdx.x;
+__device__ __forceinline__ void rope_append_block(const PrepareArgs& a, int t, float* red) {
   const int tid = threadIdx.x;
+  const int64_t slot = a.slots[t];
   int pos = a.positions[t];
   pos = pos < 0 ? 0 : (pos >= a.max_pos ? a.max_pos - 1 : pos);
   const float* cs = a.cos_sin + (int64_t)pos * 64;
+  // Pair p of the token uses frequency p % 32; a thread's pairs are tid +
+  // 256 k, so all of them use frequency tid % 32.
+  const float c = cs[tid & 31], s = cs[32 + (tid & 31)];
 
   const uint32_t* qin = reinterpret_cast<const uint32_t*>(a.q_rope_in + (int64_t)t * a.H * 64);
   uint32_t* qout = reinterpret_cast<uint32_t*>(a.q_rope_out + (int64_t)t * a.H * 64);
-  for (int p = tid; p < a.H * 32; p += 256) {
-    const int i = p & 31;
-    qout[p] = rope_pair(qin[p], cs[i], cs[32 + i]);
-  }
+  const int npairs = a.H * 32;
+#pragma unroll 4
+  for (int p = tid; p < npairs; p += 256) qout[p] = rope_pair(qin[p], c, s);
 
-  const int64_t slot = a.slots[t];
   if (slot < 0 || slot >= a.num_slots) return;  // uniform in the block
   const uint32_t ckv = reinterpret_cast<const uint32_t*>(a.c_kv_new + (int64_t)t * 512)[tid];
   uint32_t kr = 0;
   if (tid < 32) {
     const uint32_t kin = reinterpret_cast<const uint32_t*>(a.k_rope_new + (int64_t)t * 64)[tid];
-    kr = rope_pair(kin, cs[tid], cs[32 + tid]);
+    kr = rope_pair(kin, c, s);
   }
   if (!a.fp8) {
     uint32_t* row = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.pool) + slot * 576);
@@ -148,15 +178,40 @@ __global__ __launch_bounds__(256) void rope_append_kernel(PrepareArgs a) {
   if (tid == 0) a.kv_scale[slot] = scale;
 }
 
+// One launch for the whole step.  Blocks 0 .. 4 H G - 1 run the absorption:
+// block b takes (head, column quarter) b % 4 H and tokens [128 g, 128 g +
+// 128) with g = b / 4 H, so that the G token groups of one weight slice run
+// on one XCD (4 H is a multiple of 8 when H is even) and read it from L2.
+// The next T blocks run the RoPE and append of one token each; the two parts
+// are independent and run side by side.
+constexpr int kAbsorbTokens = 128;
+
+__global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[32 * kQStride];
+  __shared__ __attribute__((aligned(16))) uint16_t os[32 * kOStride];
+  const int blk = blockIdx.x;
+  const int nhq = 4 * a.H;
+  const int nabs = nhq * ((a.T + kAbsorbTokens - 1) / kAbsorbTokens);
+  if (blk < nabs) {
+    const int g = blk / nhq;
+    const int tb = g * kAbsorbTokens;
+    const int te = tb + kAbsorbTokens < a.T ? tb + kAbsorbTokens : a.T;
+    q_absorb_block(a.q_nope, a.w_kc_t, a.q_nope_absorbed, a.T, a.H, blk - g * nhq, tb, te,
+                   qs, os);
+  } else {
+    rope_append_block(a, blk - nabs, red);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prepare(const PrepareArgs& args, hipStream_t stream) {
   if (args.T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(q_absorb_kernel, dim3((unsigned)args.H * 4), dim3(256), 0, stream,
-                     args.q_nope, args.w_kc_t, args.q_nope_absorbed, args.T, args.H);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rope_append_kernel, dim3((unsigned)args.T), dim3(256), 0, stream, args);
+  const int64_t grid =
+      4 * (int64_t)args.H * ((args.T + kAbsorbTokens - 1) / kAbsorbTokens) + args.T;
+  if (grid > (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)grid), dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 """Seeded synthetic inputs for absorbed MLA decode.
 
-This package builds inputs only: page tables, pools, queries, scales.  It holds
+This package builds inputs only: page tables, pools, queries, scales, and
+the inputs of the prepare step (weights, new rows, a RoPE cos / sin table).  It holds
 none of the attention arithmetic, so both the GPU path's tests and the CPU
 oracle can consume the same tensors without sharing any computation.
 """
@@ -16,4 +17,6 @@ from .gen import (  # noqa: F401
     ragged_lengths,
     softmax_scale_default,
     kv_bytes_per_token,
+    PREPARE_CONFIGS,
+    prepare_inputs,
 )

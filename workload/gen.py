@@ -315,3 +315,41 @@ def config_inputs(cfg_id: int, device="cpu", dcp_rank: int = 0, batch: int | Non
     return make_inputs(cfg_id, c["seq_lens"], c["q_len"], c["num_heads"], c["kv_dtype"],
                        device=device, dcp_size=c.get("dcp_size", 1), dcp_rank=dcp_rank,
                        kv_std=kv_std, name=c["name"])
+
+
+# Inputs of the MLA prepare step (the T = B * q_len new tokens of a decode
+# step): seeded like the decode workloads, with a RoPE cos / sin table of
+# the usual geometric frequencies (base 10000) over max_pos positions.
+PREPARE_CONFIGS = {
+    "mtp": dict(name="prepare-mtp-80x96-fp8", T=16 * 5, H=96, kv_dtype="fp8"),
+    "dcp8": dict(name="prepare-dcp8-640x96-fp8", T=128 * 5, H=96, kv_dtype="fp8"),
+    "standard": dict(name="prepare-standard-32x128-bf16", T=32, H=128, kv_dtype="bf16"),
+}
+
+
+def prepare_inputs(key: str, device="cpu", num_slots: int = 1 << 18, max_pos: int = 1 << 17):
+    """Tensors of one mla_prepare call for PREPARE_CONFIGS[key]."""
+    c = PREPARE_CONFIGS[key]
+    T, H, kv = c["T"], c["H"], c["kv_dtype"]
+    rng = _np_rng(200, 0, sum(map(ord, key)))
+
+    def bf16(shape, std):
+        return torch.from_numpy((rng.standard_normal(shape) * std).astype(np.float32)).to(torch.bfloat16)
+    x = dict(q_nope=bf16((T, H, 128), 1.0), q_rope_in=bf16((T, H, 64), 1.0),
+             w_kc_t=bf16((H, 512, 128), 0.05), c_kv_new=bf16((T, 512), 0.5),
+             k_rope_new=bf16((T, 64), 1.0))
+    x["positions"] = torch.from_numpy(rng.integers(0, max_pos, T).astype(np.int32))
+    inv = 10000.0 ** (-np.arange(32) / 32.0)
+    ang = np.arange(max_pos)[:, None] * inv[None, :]
+    x["cos_sin"] = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32))
+    x["slots"] = torch.from_numpy(rng.permutation(num_slots)[:T].astype(np.int32))
+    if kv == "bf16":
+        x["kv_pool"] = torch.zeros((num_slots, 576), dtype=torch.bfloat16)
+        x["kv_scale"] = None
+    else:
+        x["kv_pool"] = torch.zeros((num_slots, 576), dtype=torch.uint8)
+        x["kv_scale"] = torch.ones(num_slots, dtype=torch.float32)
+    out = {k: (v.to(device) if v is not None else None) for k, v in x.items()}
+    out.update(name=c["name"], T=T, H=H, kv_dtype=kv)
+    return out
+
