@@ -29,7 +29,9 @@ The formula itself is never written on the pages; the readings taken where
 they are silent are listed in the module docstring of ``mla_ref``.
 
 ``prepare_ref`` is the oracle of the step before attention (Q absorption,
-RoPE, KV append); its readings are in its own module docstring.
+RoPE, KV append), ``project_ref`` that of the step after it (the LSE merge
+followed by the w_vc up-projection); their readings are in their own module
+docstrings.
 """
 
 from .mla_ref import (  # noqa: F401
@@ -61,4 +63,8 @@ from .prepare_ref import (  # noqa: F401
     fp8_quantise_rows,
     kv_append_ref,
     mla_prepare_ref,
+)
+from .project_ref import (  # noqa: F401
+    vc_project_ref,
+    lse_combine_project_ref,
 )
