@@ -381,12 +381,35 @@ def run_dcp_full(args, dev):
     def combine():
         mla.lse_combine(part_o, part_lse, out=out, lse=lse, stream=stream)
 
+    # The same merge fused with the w_vc up-projection (512 -> 128 per head,
+    # random bf16 weights of that shape): the merged latent O is not stored.
+    T_tok, H = x0.batch * x0.q_len, x0.num_heads
+    gen = torch.Generator(device=dev).manual_seed(4)
+    w_vc_t = (torch.randn((H, 128, 512), generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+    out_v = torch.empty((T_tok, H, 128), dtype=torch.bfloat16, device=dev)
+    po4 = part_o.view(W, T_tok, H, 512)
+    pl3 = part_lse.view(W, T_tok, H)
+
+    def combine_project():
+        mla.lse_combine_project(po4, pl3, w_vc_t, out_v=out_v, lse=lse, stream=stream)
+
+    # Unfused, for comparison: the projection of the combine's stored O (the
+    # same kernel with one part of LSE 0).
+    o1 = out.view(1, T_tok, H, 512)
+    l1 = torch.zeros((1, T_tok, H), dtype=torch.float32, device=dev)
+    lse_1 = torch.empty((T_tok, H), dtype=torch.float32, device=dev)
+
+    def project_only():
+        mla.lse_combine_project(o1, l1, w_vc_t, out_v=out_v, lse=lse_1, stream=stream)
+
     def full():
         for r in range(W):
             shard(r)
         combine()
+        combine_project()
+        project_only()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(W + 2)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(W + 4)] for _ in range(args.steps)]
     queue_ahead(full, args.steps, args.warmup)
     for k in range(args.steps):
         ev[k][0].record(stream)
@@ -395,12 +418,19 @@ def run_dcp_full(args, dev):
             ev[k][r + 1].record(stream)
         combine()
         ev[k][W + 1].record(stream)
+        combine_project()
+        ev[k][W + 2].record(stream)
+        project_only()
+        ev[k][W + 3].record(stream)
     torch.cuda.synchronize()
     per_shard = np.array([[ev[k][r].elapsed_time(ev[k][r + 1]) for r in range(W)]
                           for k in range(args.steps)]) * 1e3
     comb = np.array([ev[k][W].elapsed_time(ev[k][W + 1]) for k in range(args.steps)]) * 1e3
     total = np.array([ev[k][0].elapsed_time(ev[k][W + 1]) for k in range(args.steps)]) * 1e3
     comb_bytes = (W + 1) * rows * (512 * 4 + 4)
+    cp = np.array([ev[k][W + 1].elapsed_time(ev[k][W + 2]) for k in range(args.steps)]) * 1e3
+    cp_bytes = W * rows * (512 * 4 + 4) + rows * (128 * 2 + 4) + H * 128 * 512 * 2
+    po_us = np.array([ev[k][W + 2].elapsed_time(ev[k][W + 3]) for k in range(args.steps)]) * 1e3
     print(json.dumps({
         "dcp": "128x100k-q5-h96-fp8 over 8 shards (p % 8 == r), all on one GPU",
         "per_shard_us_median": round(float(np.median(per_shard)), 1),
@@ -408,6 +438,12 @@ def run_dcp_full(args, dev):
         "sum_8_shards_plus_combine_us": round(float(np.median(total)), 1),
         "combine_us": round(float(np.median(comb)), 1),
         "combine_hbm_tb_per_s": round(comb_bytes / (float(np.median(comb)) * 1e-6) / 1e12, 3),
+        "combine_project_us": round(float(np.median(cp)), 1),
+        "combine_project_hbm_tb_per_s": round(cp_bytes / (float(np.median(cp)) * 1e-6) / 1e12, 3),
+        "combine_project_note": "the same 8-part merge fused with the w_vc up-projection "
+                                "(512 -> 128 per head, bf16 out); the merged fp32 O is not stored",
+        "unfused_combine_then_project_us": round(float(np.median(comb)) + float(np.median(po_us)), 1),
+        "project_only_us": round(float(np.median(po_us)), 1),
         "context_b200_us": {"per_shard_attn_mqa": 826.0, "dcp_pack_plus_lse_combine": 30.0},
         "steps": args.steps, "warmup": args.warmup}), flush=True)
 

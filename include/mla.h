@@ -235,6 +235,35 @@ mla_status mla_prepare(int32_t num_tokens, int32_t num_heads, int32_t kv_dtype,
                        void* q_nope_absorbed, void* q_rope_out, void* kv_pool, float* kv_scale,
                        int64_t num_slots, void* stream);
 
+/*
+ * LSE merge fused with the w_vc up-projection: the step after mla_decode
+ * (DP16-vs-DP2 page: kv_b_proj is absorbed into w_kc / w_vc, so w_vc is
+ * applied after attention in the latent space; section "MLA": the per-shard
+ * (O, LSE) are merged by LSE, dcp_lse_combine).  For every token t and head
+ * h, the num_parts partial results are merged as in mla_lse_combine and the
+ * merged latent O (rounded to bf16, never stored) is projected:
+ *
+ *   out[t, h, n] = sum_k O[t, h, k] * w_vc[h, k, n]   (k < 512, n < 128),
+ *
+ * with fp32 accumulation, rounded to bf16.  A row whose parts all have
+ * LSE = -inf gives out = 0 and LSE = -inf.  With num_parts = 1 this is the
+ * plain projection of one decode output.
+ *
+ *   part_o:    fp32 [num_parts, T, H, 512] device (e.g. the stacked outputs of
+ *              the DCP shards' mla_decode calls).
+ *   part_lse:  fp32 [num_parts, T, H] device.
+ *   w_vc_t:    bf16 [H, 128, 512] device: every head's w_vc transposed, element
+ *              (h, n, k) = w_vc[h, k, n] (laid out once when the weights are
+ *              loaded, so that the MFMA operand reads rows with k contiguous).
+ *   out_v:     bf16 [T, H, 128] device output (the value heads o_proj reads).
+ *   lse:       fp32 [T, H] device output of the merged LSE, or NULL.
+ *   num_parts >= 1, num_tokens >= 0 (0: nothing is enqueued), num_heads >= 1;
+ *   16-byte aligned pointers (lse 4-byte).
+ */
+mla_status mla_lse_combine_project(const float* part_o, const float* part_lse, int32_t num_parts,
+                                   int32_t num_tokens, int32_t num_heads, const void* w_vc_t,
+                                   void* out_v, float* lse, void* stream);
+
 /* Static description of a status code. */
 const char* mla_status_string(mla_status status);
 

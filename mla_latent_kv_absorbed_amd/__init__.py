@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     lse_combine,
+    lse_combine_project,
     make_desc,
     make_plan,
     plan_max_bytes,

@@ -69,6 +69,8 @@ def load_library():
     lib.mla_prepare.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                 vp, i64, vp]
     lib.mla_prepare.restype = i32
+    lib.mla_lse_combine_project.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.mla_lse_combine_project.restype = i32
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
     _LIB = lib
@@ -301,3 +303,29 @@ def prepare(q_nope, q_rope_in, w_kc_t, c_kv_new, k_rope_new, positions, cos_sin,
     if st != MLA_OK:
         raise MlaError("mla_prepare failed", st)
     return q_nope_absorbed, q_rope_out
+
+
+def lse_combine_project(part_o, part_lse, w_vc_t, out_v=None, lse=None, stream=None):
+    """mla_lse_combine_project: merge [P, T, H, 512] / [P, T, H] partials by LSE
+    and project the merged rows with w_vc_t [H, 128, 512] (bf16).  Returns
+    (out_v bf16 [T, H, 128], lse fp32 [T, H])."""
+    import torch
+    if part_o.dim() != 4 or part_o.shape[-1] != 512 or part_o.dtype != torch.float32 or \
+            tuple(part_lse.shape) != tuple(part_o.shape[:3]) or part_lse.dtype != torch.float32:
+        raise MlaError("part_o must be fp32 [P, T, H, 512] and part_lse fp32 [P, T, H]")
+    P, T, H = (int(v) for v in part_o.shape[:3])
+    if tuple(w_vc_t.shape) != (H, 128, 512) or w_vc_t.dtype != torch.bfloat16:
+        raise MlaError("w_vc_t must be bf16 [H, 128, 512]")
+    for name, t in (("part_o", part_o), ("part_lse", part_lse), ("w_vc_t", w_vc_t)):
+        if not t.is_contiguous() or t.device != part_o.device:
+            raise MlaError(f"{name} must be contiguous on {part_o.device}")
+    if out_v is None:
+        out_v = torch.empty((T, H, 128), dtype=torch.bfloat16, device=part_o.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=part_o.device)
+    st = load_library().mla_lse_combine_project(_ptr(part_o), _ptr(part_lse), P, T, H,
+                                                _ptr(w_vc_t), _ptr(out_v), _ptr(lse),
+                                                _stream(stream))
+    if st != MLA_OK:
+        raise MlaError("mla_lse_combine_project failed", st)
+    return out_v, lse

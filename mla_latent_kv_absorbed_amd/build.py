@@ -9,7 +9,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "mla_kernels.hip"), os.path.join(HERE, "csrc", "mla_prepare.hip"),
-           os.path.join(HERE, "csrc", "mla_api.cpp")]
+           os.path.join(HERE, "csrc", "mla_project.hip"), os.path.join(HERE, "csrc", "mla_api.cpp")]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-I", os.path.join(ROOT, "include"),

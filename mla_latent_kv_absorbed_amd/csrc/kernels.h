@@ -55,4 +55,10 @@ struct PrepareArgs {
 
 hipError_t launch_prepare(const PrepareArgs& args, hipStream_t stream);
 
+// LSE merge of [P, T, H, 512] fp32 parts fused with the w_vc up-projection:
+// out bf16 [T, H, 128], lse fp32 [T, H] (may be null).
+hipError_t launch_combine_project(const float* part_o, const float* part_lse, int nparts, int T,
+                                  int H, const uint16_t* w_vc_t, uint16_t* out, float* lse,
+                                  hipStream_t stream);
+
 }  // namespace mla

@@ -144,6 +144,20 @@ mla_status mla_prepare(int32_t num_tokens, int32_t num_heads, int32_t kv_dtype,
   return MLA_OK;
 }
 
+mla_status mla_lse_combine_project(const float* part_o, const float* part_lse, int32_t num_parts,
+                                   int32_t num_tokens, int32_t num_heads, const void* w_vc_t,
+                                   void* out_v, float* lse, void* stream) {
+  if (num_parts < 1 || num_tokens < 0 || num_heads < 1) return MLA_ERR_INVALID_ARG;
+  for (const void* p : {(const void*)part_o, (const void*)part_lse, w_vc_t, (const void*)out_v})
+    if (!p || !aligned16(p)) return MLA_ERR_INVALID_ARG;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return MLA_ERR_INVALID_ARG;
+  if (launch_combine_project(part_o, part_lse, num_parts, num_tokens, num_heads,
+                             static_cast<const uint16_t*>(w_vc_t), static_cast<uint16_t*>(out_v),
+                             lse, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_status_string(mla_status s) {
   switch (s) {
     case MLA_OK: return "ok";

@@ -172,3 +172,15 @@ def test_prepare_rejects_bad_arguments_on_host():
     assert call(scale=f + 2) == -1                   # misaligned scales
     # q_rope_out aliasing q_rope_in
     assert lib.mla_prepare(4, 2, 0, f, g, f, f, f, f, f, 8, f, f, g, f, None, 16, None) == -1
+
+
+def test_combine_project_rejects_bad_arguments_on_host():
+    lib = mla.load_library()
+    f = 1 << 20
+    assert lib.mla_lse_combine_project(f, f, 2, 0, 4, f, f, f, None) == 0     # T = 0
+    assert lib.mla_lse_combine_project(f, f, 0, 4, 4, f, f, f, None) == -1    # no parts
+    assert lib.mla_lse_combine_project(f, f, 2, -1, 4, f, f, f, None) == -1
+    assert lib.mla_lse_combine_project(f, f, 2, 4, 0, f, f, f, None) == -1
+    assert lib.mla_lse_combine_project(None, f, 2, 4, 4, f, f, f, None) == -1
+    assert lib.mla_lse_combine_project(f, f, 2, 4, 4, f + 8, f, f, None) == -1
+    assert lib.mla_lse_combine_project(f, f, 2, 4, 4, f, f, f + 2, None) == -1
