@@ -26,6 +26,7 @@
 
 #include "mla.h"
 #include "kernels.h"
+#include "kernels_step.h"
 #include "plan_layout.h"
 
 

@@ -20,7 +20,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "kernels.h"
+#include "kernels_step.h"
 
 namespace mla {
 namespace {

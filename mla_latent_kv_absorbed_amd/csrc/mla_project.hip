@@ -23,7 +23,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "kernels.h"
+#include "kernels_step.h"
 
 namespace mla {
 namespace {
