@@ -172,6 +172,34 @@ def test_dcp_shards_merge_to_full_context(kv):
     check(mo, ml, o_full, l_full, tag=f"{kv} 8-shard merge vs full context")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_other_dcp_widths_merge_to_full_context(kv, W):
+    # Shard counts other than 8 (3 does not divide the page size): every
+    # shard against the oracle, and their LSE merge against full context.
+    full = make_inputs(64 + W, [900, 301, 7, 5], 5, 24, kv, kv_std=0.1 if kv == "bf16" else 1.0)
+    o_full, l_full = oracle(full)
+    parts_o, parts_l = [], []
+    for r in range(W):
+        s = shard_from_full(full, W, r)
+        out, lse = gpu_decode(s)
+        check(out, lse, *oracle(s), tag=f"{kv} W{W} shard {r}")
+        parts_o.append(out)
+        parts_l.append(lse)
+    mo, ml = mla.lse_combine(torch.stack(parts_o).contiguous(), torch.stack(parts_l).contiguous())
+    torch.cuda.synchronize()
+    check(mo, ml, o_full, l_full, tag=f"{kv} {W}-shard merge vs full context")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_largest_q_len_and_many_row_groups(kv):
+    # q_len 8 (the largest) x 128 heads = 1024 rows: 8 row groups per request.
+    x = make_inputs(66, [700, 64, 8], 8, 128, kv, kv_std=0.1 if kv == "bf16" else 1.0)
+    for splits in (0, 3):
+        out, lse = gpu_decode(x, force_splits=splits)
+        check(out, lse, *oracle(x), tag=f"{kv} q8 h128 splits {splits}")
+
+
 def test_lse_combine_edge_cases():
     rng = np.random.default_rng(4)
     P, rows = 5, 300
