@@ -451,8 +451,10 @@ def run_dcp_full(args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first: the first few dozen launches run slower while "
+                         "the GPU clocks settle")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="mtp")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=4)
