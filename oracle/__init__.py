@@ -28,10 +28,12 @@ Sources (all on the page "Kimi K3 decode: DP16 vs DP2 x DCP8" and the page
 The formula itself is never written on the pages; the readings taken where
 they are silent are listed in the module docstring of ``mla_ref``.
 
-``prepare_ref`` is the oracle of the step before attention (Q absorption,
-RoPE, KV append), ``project_ref`` that of the step after it (the LSE merge
-followed by the w_vc up-projection); their readings are in their own module
-docstrings.
+``fp4_ref`` defines the FP4 KV rows (e2m1 codes with one power-of-two
+scale per 16 elements; VRAM page, "KV ledger" and "cell_size" sections) and
+their quantiser.  ``prepare_ref`` is the oracle of the step before
+attention (Q absorption, RoPE, KV append), ``project_ref`` that of the step
+after it (the LSE merge followed by the w_vc up-projection); their readings
+are in their own module docstrings.
 """
 
 from .mla_ref import (  # noqa: F401
@@ -63,6 +65,14 @@ from .prepare_ref import (  # noqa: F401
     fp8_quantise_rows,
     kv_append_ref,
     mla_prepare_ref,
+)
+from .fp4_ref import (  # noqa: F401
+    E2M1_TABLE,
+    e2m1_decode_table,
+    e2m1_encode,
+    decode_fp4_rows,
+    block_exponent_of,
+    fp4_quantise_rows,
 )
 from .project_ref import (  # noqa: F401
     vc_project_ref,

@@ -12,7 +12,8 @@ What is computed, for request b, draft position i in [0, q) and head h:
    tokens; section "problem: how to split" for slot p -> rank p % 8.)
 2. Keys.  slot = req_to_token[b, j]; the key is the whole 576-wide latent row
    [c_kv (512) | k_rope (64)] of that slot, decoded exactly to float64: BF16
-   bits, or OCP e4m3fn codes times the slot's fp32 scale.  (VRAM page,
+   bits, OCP e4m3fn codes times the slot's fp32 scale, or FP4 codes times
+   their block scale (format and readings in fp4_ref).  (VRAM page,
    "KV ledger" MLA bullet and the "cell_size" MLA pool shape
    (size + page_size, 1, kv_lora_rank + qk_rope_head_dim).)
 3. Values.  The first 512 elements of the same row (the latent c_kv).
@@ -40,6 +41,8 @@ also under DCP.
 from __future__ import annotations
 
 import numpy as np
+
+from .fp4_ref import decode_fp4_rows
 
 D_C = 512  # kv_lora_rank: width of the latent c_kv
 D_R = 64  # qk_rope_head_dim: width of the decoupled RoPE key
@@ -112,6 +115,8 @@ def dequant_rows(pool: np.ndarray, kv_scale, slots: np.ndarray,
     if kv_dtype == "fp8":
         scale = np.asarray(kv_scale, dtype=np.float32)[slots].astype(np.float64)
         return E4M3FN_TABLE[raw.astype(np.intp)] * scale[:, None]
+    if kv_dtype == "fp4":
+        return decode_fp4_rows(raw)
     raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
 
 
@@ -152,8 +157,9 @@ def mla_decode_ref(q_nope, q_rope, pool, kv_scale, req_to_token, seq_lens,
     Arguments are the stored bit patterns, as numpy arrays:
       q_nope        uint16 [B, q, H, 512]  BF16 bits of the absorbed no-RoPE query
       q_rope        uint16 [B, q, H, 64]   BF16 bits of the RoPE query
-      pool          uint16 [S, 576] (BF16 bits) or uint8 [S, 576] (e4m3fn codes)
-      kv_scale      float32 [S] for FP8, ignored for BF16
+      pool          uint16 [S, 576] (BF16 bits), uint8 [S, 576] (e4m3fn codes) or
+                    uint8 [S, 336] (FP4 rows, format in fp4_ref)
+      kv_scale      float32 [S] for FP8, ignored otherwise
       req_to_token  int32 [B, >= local length]; column j is local index j
       seq_lens      int [B]; global lengths L_b including the q drafts
     p_range=(lo, hi) keeps only global positions lo <= p < hi (a partial).

@@ -34,6 +34,13 @@ D_K = 576
 
 BF16_NAN_BITS = 0x7FC0
 E4M3FN_NAN_CODE = 0x7F
+# FP4 rows: 576 e2m1 codes packed two per byte (element 2 i in the low
+# nibble of byte i), 36 block-scale bytes (power-of-two exponents with bias
+# 127, one per 16 elements), 12 bytes of zero padding.
+FP4_ROW_BYTES = 336
+FP4_CODE_BYTES = 288
+FP4_POISON_CODES = 0x77     # e2m1 6.0 in both nibbles
+FP4_POISON_SCALE = 0xFF     # not a valid scale code
 
 # Tensor ids for the seed sequences.
 _T_LENGTHS, _T_PAGES, _T_SCALE, _T_KV, _T_QNOPE, _T_QROPE, _T_PLANT = range(7)
@@ -45,7 +52,10 @@ def softmax_scale_default() -> float:
 
 
 def kv_bytes_per_token(kv_dtype: str) -> int:
-    """Algorithmic KV bytes read per visible token: 576 elements (+ fp32 scale for FP8)."""
+    """Algorithmic KV bytes read per visible token: 576 elements (+ fp32 scale
+    for FP8); FP4 rows are 336 bytes (288 of codes, 36 block scales, padding)."""
+    if kv_dtype == "fp4":
+        return FP4_ROW_BYTES
     return D_K * 2 if kv_dtype == "bf16" else D_K * 1 + 4
 
 
@@ -79,13 +89,13 @@ class DecodeInputs:
     batch: int
     q_len: int
     num_heads: int
-    kv_dtype: str  # "bf16" | "fp8"
+    kv_dtype: str  # "bf16" | "fp8" | "fp4"
     page_size: int
     seq_lens: np.ndarray  # int64 [B], global lengths including the q drafts
     local_lens: np.ndarray  # int64 [B], table columns used on this shard
     q_nope: torch.Tensor  # bf16 [B, q, H, 512]
     q_rope: torch.Tensor  # bf16 [B, q, H, 64]
-    pool: torch.Tensor  # bf16 [S, 576] or uint8 [S, 576]
+    pool: torch.Tensor  # bf16 [S, 576], uint8 [S, 576] (e4m3fn) or uint8 [S, 336] (FP4)
     kv_scale: torch.Tensor | None  # float32 [S] (FP8 only)
     req_to_token: torch.Tensor  # int32 [B, stride]
     softmax_scale: float
@@ -170,6 +180,22 @@ def _fill_values(shape, gen, device, dtype_out: str, std: float) -> torch.Tensor
     return out
 
 
+def _fill_fp4(rows: int, gen, device, exp_lo: int, exp_hi: int) -> torch.Tensor:
+    """FP4 rows: uniformly random codes, block-scale exponents uniform in
+    [exp_lo, exp_hi] (as codes 127 + e), zero padding."""
+    out = torch.zeros((rows, FP4_ROW_BYTES), dtype=torch.uint8, device=device)
+    chunk = 1 << 18
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        out[r0:r1, :FP4_CODE_BYTES] = torch.randint(
+            0, 256, (r1 - r0, FP4_CODE_BYTES), generator=gen, device=device,
+            dtype=torch.int32).to(torch.uint8)
+        out[r0:r1, FP4_CODE_BYTES:FP4_CODE_BYTES + 36] = torch.randint(
+            127 + exp_lo, 127 + exp_hi + 1, (r1 - r0, 36), generator=gen, device=device,
+            dtype=torch.int32).to(torch.uint8)
+    return out
+
+
 def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str,
                 page_size: int = 64, device="cpu", dcp_size: int = 1, dcp_rank: int = 0,
                 q_std: float = 0.1, kv_std: float = 0.1, scale_lo: float = 0.01,
@@ -190,7 +216,12 @@ def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str
     table, num_slots, used = _page_table(cfg_id, local, page_size, extra)
 
     kv_gen = _torch_gen(cfg_id, _T_KV, extra, device)
-    pool = _fill_values((num_slots, D_K), kv_gen, device, kv_dtype, kv_std)
+    if kv_dtype == "fp4":
+        # Elements up to 6 * 2^-4; typical magnitudes near those of the BF16
+        # pools (N(0, 1) * 0.1).
+        pool = _fill_fp4(num_slots, kv_gen, device, -6, -4)
+    else:
+        pool = _fill_values((num_slots, D_K), kv_gen, device, kv_dtype, kv_std)
     kv_scale = None
     if kv_dtype == "fp8":
         sc = _np_rng(cfg_id, _T_SCALE, extra).uniform(scale_lo, scale_hi, size=num_slots)
@@ -208,9 +239,16 @@ def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str
         qr[..., 0] = 100.0
         if kv_dtype == "bf16":
             pool[:, D_C] = 40.0
+        elif kv_dtype == "fp4":
+            # Element 512 (low nibble of byte 256) = 6 * 2^3 = 48; the rest of
+            # its block scales up by 2^3 with it.
+            pool[:, D_C // 2] = (pool[:, D_C // 2] & 0xF0) | 0x7
+            pool[:, FP4_CODE_BYTES + D_C // 16] = 127 + 3
         else:
             pool[:, D_C] = 0x7E  # e4m3fn 448
     elif variant == "planted":
+        if kv_dtype == "fp4":
+            raise ValueError("the planted variant is defined for BF16 and FP8 pools")
         rng = _np_rng(cfg_id, _T_PLANT, extra)
         q0 = torch.cat([qn[:, 0, 0].float(), qr[:, 0, 0].float()], dim=-1).cpu()  # [B, 576]
         for b in range(B):
@@ -227,12 +265,7 @@ def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str
                 vals = (direction[None, :] * 40.0 / sc[:, None]).clamp(-448, 448)
                 pool[slots.to(device)] = vals.to(torch.float8_e4m3fn).view(torch.uint8).to(device)
 
-    unused = torch.from_numpy(~used).to(device)
-    if kv_dtype == "bf16":
-        pool.view(torch.int16)[unused] = BF16_NAN_BITS
-    else:
-        pool[unused] = E4M3FN_NAN_CODE
-        kv_scale[unused] = float("nan")
+    _poison(pool, kv_scale, torch.from_numpy(~used).to(device), kv_dtype)
 
     return DecodeInputs(
         batch=B, q_len=q_len, num_heads=num_heads, kv_dtype=kv_dtype, page_size=page_size,
@@ -240,6 +273,19 @@ def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str
         kv_scale=kv_scale, req_to_token=torch.from_numpy(table).to(device),
         softmax_scale=softmax_scale_default(), dcp_size=dcp_size, dcp_rank=dcp_rank,
         name=name, meta=dict(cfg_id=cfg_id, variant=variant))
+
+
+def _poison(pool, kv_scale, unused, kv_dtype: str) -> None:
+    """Fill the slots no table entry references with values that would show."""
+    if kv_dtype == "bf16":
+        pool.view(torch.int16)[unused] = BF16_NAN_BITS
+    elif kv_dtype == "fp4":
+        pool[unused, :FP4_CODE_BYTES] = FP4_POISON_CODES
+        pool[unused, FP4_CODE_BYTES:FP4_CODE_BYTES + 36] = FP4_POISON_SCALE
+    else:
+        pool[unused] = E4M3FN_NAN_CODE
+        if kv_scale is not None:
+            kv_scale[unused] = float("nan")
 
 
 def shard_from_full(full: DecodeInputs, dcp_size: int, dcp_rank: int,
@@ -254,7 +300,8 @@ def shard_from_full(full: DecodeInputs, dcp_size: int, dcp_rank: int,
     local = local_lengths(full.seq_lens, W, r)
     table, num_slots, used = _page_table(cfg_id, local, full.page_size, 1000 + r)
     dev = full.pool.device
-    pool = torch.empty((num_slots, D_K), dtype=full.pool.dtype, device=dev)
+    pool = torch.empty((num_slots,) + tuple(full.pool.shape[1:]), dtype=full.pool.dtype,
+                       device=dev)
     kv_scale = None if full.kv_scale is None else torch.full(
         (num_slots,), float("nan"), dtype=torch.float32, device=dev)
     full_table = full.req_to_token.cpu().numpy()
@@ -268,11 +315,7 @@ def shard_from_full(full: DecodeInputs, dcp_size: int, dcp_rank: int,
         pool[dst] = full.pool[src]
         if kv_scale is not None:
             kv_scale[dst] = full.kv_scale[src]
-    unused = torch.from_numpy(~used).to(dev)
-    if full.kv_dtype == "bf16":
-        pool.view(torch.int16)[unused] = BF16_NAN_BITS
-    else:
-        pool[unused] = E4M3FN_NAN_CODE
+    _poison(pool, kv_scale, torch.from_numpy(~used).to(dev), full.kv_dtype)
     return DecodeInputs(
         batch=full.batch, q_len=full.q_len, num_heads=full.num_heads, kv_dtype=full.kv_dtype,
         page_size=full.page_size, seq_lens=full.seq_lens.copy(), local_lens=local,
