@@ -41,9 +41,11 @@ def mfma_peak_tflops(kv_dtype: str) -> float:
     products on bf16 MFMAs.  FP8 KV: the c_kv parts of Q.K and P.V (2 * 512
     + 2 * 512 of the 2176 FLOP per row and token) run on e4m3 MFMAs, the
     RoPE part (2 * 64) on bf16 MFMAs, so the floor is the sum of the two
-    times and the effective peak 2176 / (2048 / 5000 + 128 / 2500).
+    times and the effective peak 2176 / (2048 / 5000 + 128 / 2500).  FP4 KV:
+    the rows are dequantized exactly to BF16 and both products run on bf16
+    MFMAs.
     """
-    if kv_dtype == "bf16":
+    if kv_dtype in ("bf16", "fp4"):
         return MFMA_BF16_PEAK_TFLOPS
     return 2176.0 / (2048.0 / MFMA_FP8_PEAK_TFLOPS + 128.0 / MFMA_BF16_PEAK_TFLOPS)
 B200_CONTEXT_US = {"mtp": 1240.0, "dcp8": 826.0}  # the pages' numbers (other hardware)
@@ -53,6 +55,8 @@ WORKLOADS = {
     "standard": 2,  # 32 x 4096, q1, h128, bf16
     "tiny": 1,      # 2 x {1024, 1536}, q1, h16, bf16
     "dcp8": 4,      # one shard of 128 x 100k over 8 shards, q5, h96, fp8
+    "mtp-fp4": 6,   # the mtp shape over an FP4 pool
+    "standard-fp4": 7,  # the standard shape over an FP4 pool
 }
 
 
@@ -595,7 +599,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if x.kv_dtype == "bf16" else "fp8_e4m3+bf16",
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3+bf16", "fp4": "fp4_e2m1+bf16"}[x.kv_dtype],
         "data": "synthetic",
         "config": {"workload": CONFIGS[cfg]["name"], "requests": x.batch,
                    "context": int(max(x.seq_lens)), "q_len": x.q_len, "heads": x.num_heads,

@@ -47,9 +47,22 @@ typedef enum {
   MLA_ERR_HIP = -4                  /* a HIP runtime call or kernel launch failed */
 } mla_status;
 
+/*
+ * KV pool formats.  FP4 (page "resident VRAM accounting", sections "KV ledger"
+ * and "cell_size": two codes per byte plus one scale per 16 elements, a
+ * little over a quarter of BF16 per token) is read as: OCP e2m1 codes and
+ * one power-of-two scale byte per 16 elements.  A token's row is 336 bytes:
+ *   bytes   0..287  the 576 codes, element 2 i in the low nibble of byte i;
+ *   bytes 288..323  block scales, byte 288 + k for elements 16 k .. 16 k + 15,
+ *                   code c meaning 2^(c - 127), valid for 63 <= c <= 191;
+ *   bytes 324..335  padding (ignored; rows stay 16-byte aligned).
+ * Element value = e2m1(code) * 2^(c - 127).  A referenced row with a scale
+ * code outside 63..191 gives an undefined result (no fault).
+ */
 typedef enum {
   MLA_KV_BF16 = 0,     /* pool element = bfloat16 */
-  MLA_KV_FP8_E4M3 = 1  /* pool element = OCP e4m3fn byte; fp32 scale per slot */
+  MLA_KV_FP8_E4M3 = 1, /* pool element = OCP e4m3fn byte; fp32 scale per slot */
+  MLA_KV_FP4_E2M1 = 2  /* 336-byte rows of e2m1 codes and block scales (above) */
 } mla_kv_dtype;
 
 /* Problem description shared by the planner and the decode call. */
@@ -110,9 +123,10 @@ mla_status mla_decode_plan(const mla_decode_desc* desc, const int32_t* seq_lens_
  *   q_rope:          bf16 [B, q_len, H, 64], contiguous, device.
  *   kv_pool:         [num_slots, 576] contiguous, device; bf16 or e4m3fn bytes
  *                    per desc.kv_dtype; row = [c_kv (512) | k_rope (64)];
+ *                    FP4: [num_slots, 336] bytes in the row format above.
  *                    1 <= num_slots <= 2^31 - 1.
  *   kv_scale:        fp32 [num_slots] for FP8 (value = e4m3fn(code) * scale),
- *                    NULL for BF16.
+ *                    ignored (may be NULL) for BF16 and FP4.
  *   req_to_token:    int32 [B, req_to_token_stride], device; column j holds the
  *                    pool slot of local index j (= position p when W == 1).
  *                    Slots outside [0, num_slots) are clamped (no fault, but the

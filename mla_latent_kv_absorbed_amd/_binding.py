@@ -16,7 +16,9 @@ import numpy as np
 
 KV_BF16 = 0
 KV_FP8 = 1
-_KV_CODES = {"bf16": KV_BF16, "fp8": KV_FP8}
+KV_FP4 = 2
+_KV_CODES = {"bf16": KV_BF16, "fp8": KV_FP8, "fp4": KV_FP4}
+FP4_ROW_BYTES = 336
 
 MLA_OK = 0
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape",
@@ -204,10 +206,15 @@ def decode(plan: Plan, q_nope, q_rope, kv_pool, kv_scale, req_to_token, seq_lens
             tuple(q_rope.shape) != (B, h["q_len"], h["num_heads"], 64):
         raise MlaError("query shapes do not match the plan")
     fp8 = h["kv_dtype"] == KV_FP8
-    want_pool = torch.uint8 if fp8 else torch.bfloat16
-    if kv_pool.dtype not in ((want_pool, torch.float8_e4m3fn) if fp8 else (want_pool,)) or \
-            kv_pool.dim() != 2 or kv_pool.shape[1] != 576:
-        raise MlaError("kv_pool must be [num_slots, 576] of the plan's dtype")
+    if h["kv_dtype"] == KV_FP4:
+        if kv_pool.dtype != torch.uint8 or kv_pool.dim() != 2 or \
+                kv_pool.shape[1] != FP4_ROW_BYTES:
+            raise MlaError(f"FP4 pools must be uint8 [num_slots, {FP4_ROW_BYTES}]")
+    else:
+        want_pool = torch.uint8 if fp8 else torch.bfloat16
+        if kv_pool.dtype not in ((want_pool, torch.float8_e4m3fn) if fp8 else (want_pool,)) or \
+                kv_pool.dim() != 2 or kv_pool.shape[1] != 576:
+            raise MlaError("kv_pool must be [num_slots, 576] of the plan's dtype")
     if fp8 and (kv_scale is None or kv_scale.dtype != torch.float32 or
                 kv_scale.numel() < kv_pool.shape[0] or kv_scale.device != dev):
         raise MlaError("FP8 pools need an fp32 kv_scale per slot on the same device")

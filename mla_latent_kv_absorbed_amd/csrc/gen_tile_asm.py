@@ -15,6 +15,7 @@ Statements (T = BF16 or FP8):
 
   MLA_QK_T_ASM       QK (first tile of a unit)
   MLA_FUSED_BF16_ASM QK of tile t+1 and PV of tile t, plus DMA
+  MLA_FUSED_BF16_NODMA_ASM  the same without the DMA (FP4 pools)
   MLA_PV_T_ASM       PV (last tile of a unit)
   FP8, pipelined one tile deeper so that the softmax runs in the MFMA shadow:
   MLA_QKSM_FP8_ASM   QK of tile t+1 and SM of tile t, plus DMA (first step)
@@ -652,6 +653,9 @@ STATEMENTS = (
     ("MLA_SMPV_FP8_ASM", dict(fp8=True, qk=False, pv=True, sm=True)),
     ("MLA_SM_FP8_ASM", dict(fp8=True, qk=False, pv=False, sm=True)),
     ("MLA_PV_FP8_ASM", dict(fp8=True, qk=False, pv=True)),
+    # FP4 pools: the BF16 tiles are dequantized in LDS, and the FP4 DMA is
+    # issued outside the statement.
+    ("MLA_FUSED_BF16_NODMA_ASM", dict(fp8=False, qk=True, pv=True)),
 )
 
 

@@ -34,6 +34,10 @@ namespace {
 
 using namespace mla;
 
+// launch_decode takes the plan's mla_kv_dtype as a KvKind.
+static_assert(kKvBf16 == MLA_KV_BF16 && kKvFp8 == MLA_KV_FP8_E4M3 && kKvFp4 == MLA_KV_FP4_E2M1,
+              "KvKind and mla_kv_dtype differ");
+
 // Fixed cost of one work unit, in token-equivalents (Q load + O write).
 constexpr int64_t kUnitOverheadTokens = 128;
 // Smallest piece worth a workgroup of its own, in token-equivalents.
@@ -50,7 +54,9 @@ mla_status check_desc(const mla_decode_desc* d) {
     return MLA_ERR_INVALID_ARG;
   if ((int64_t)d->q_len * d->num_heads > (1 << 20)) return MLA_ERR_INVALID_ARG;
   if (d->page_size < 1) return MLA_ERR_INVALID_ARG;
-  if (d->kv_dtype != MLA_KV_BF16 && d->kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARG;
+  if (d->kv_dtype != MLA_KV_BF16 && d->kv_dtype != MLA_KV_FP8_E4M3 &&
+      d->kv_dtype != MLA_KV_FP4_E2M1)
+    return MLA_ERR_INVALID_ARG;
   if (d->dcp_size < 1 || d->dcp_rank < 0 || d->dcp_rank >= d->dcp_size)
     return MLA_ERR_INVALID_ARG;
   if (d->num_cus < 0 || d->force_splits < 0) return MLA_ERR_INVALID_ARG;
@@ -453,9 +459,9 @@ mla_status mla_decode_attend(const void* plan_host, const void* plan_device, con
                                     num_slots, req_to_token, req_to_token_stride, seq_lens,
                                     softmax_scale, workspace, workspace_bytes, out, lse, &a, &h);
   if (st != MLA_OK) return st;
-  const bool fp8 = h->kv_dtype == MLA_KV_FP8_E4M3;
   const bool paged = (h->page_size % kTile) == 0;
-  if (launch_decode(fp8, paged, h->num_wgs, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_decode(h->kv_dtype, paged, h->num_wgs, a, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_O_MAX, TOL_O_REL, TOL_LSE = 2e-2, 1e-2, 1e-3
 DEV = "cuda"
+KV_DTYPES = ["bf16", "fp8", "fp4"]
 
 
 def oracle(x, reqs=None, **kw):
@@ -71,7 +72,7 @@ def test_tiny_workload_exact_config():
     check(out, lse, *oracle(x), tag="tiny 2x{1024,1536} q1 h16 bf16")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", KV_DTYPES)
 @pytest.mark.parametrize("q,H", [(1, 128), (5, 96), (2, 16), (3, 40)])
 def test_small_shapes(kv, q, H):
     lens = [700, 33, q, 1000] if q > 1 else [700, 33, 1, 1000]
@@ -80,7 +81,7 @@ def test_small_shapes(kv, q, H):
     check(out, lse, *oracle(x), tag=f"{kv} q{q} h{H} lens {lens}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", KV_DTYPES)
 @pytest.mark.parametrize("q,H,splits", [(1, 8, 5), (5, 96, 9), (2, 112, 3), (5, 96, 0)])
 def test_rows_past_the_request_end(kv, q, H, splits):
     # Row groups whose last waves hold no valid row (8 rows: waves 1-3 of
@@ -94,18 +95,20 @@ def test_rows_past_the_request_end(kv, q, H, splits):
     check(out, lse, *oracle(x), tag=f"{kv} q{q} h{H} splits {splits} lens {lens}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", KV_DTYPES)
 @pytest.mark.parametrize("variant", ["qx30", "planted", "offset"])
 @pytest.mark.parametrize("q", [1, 5])
 @pytest.mark.parametrize("splits", [1, 2, 7, 40])
 def test_peaked_variants_and_forced_splits(kv, variant, q, splits):
+    if kv == "fp4" and variant == "planted":
+        pytest.skip("the planted variant is defined for BF16 and FP8 pools only")
     x = make_inputs(50, [1300, 257], q, 32, kv, variant=variant,
                     kv_std=0.1 if kv == "bf16" else 1.0)
     out, lse = gpu_decode(x, force_splits=splits)
     check(out, lse, *oracle(x), tag=f"{kv} {variant} q{q} splits {splits}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", KV_DTYPES)
 @pytest.mark.parametrize("page_size", [1, 16, 64, 128])
 def test_page_sizes_and_general_tables(kv, page_size):
     # page_size 1 and 16 exercise the per-token table path.
@@ -115,7 +118,7 @@ def test_page_sizes_and_general_tables(kv, page_size):
     check(out, lse, *oracle(x), tag=f"{kv} page {page_size}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", KV_DTYPES)
 def test_edge_lengths(kv):
     # seq_len == q_len (one visible token for draft 0), exact tile multiples, +1 tails.
     lens = [5, 6, 32, 33, 64, 65, 95, 96, 97]
@@ -125,7 +128,7 @@ def test_edge_lengths(kv):
         check(out, lse, *oracle(x), tag=f"{kv} edge lengths splits {fs}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", KV_DTYPES)
 def test_planner_cuts_match_unsplit(kv):
     x = make_inputs(62, [3000, 100, 4097], 5, 96, kv, kv_std=0.1 if kv == "bf16" else 1.0)
     o1, l1 = gpu_decode(x, force_splits=1)
@@ -135,7 +138,7 @@ def test_planner_cuts_match_unsplit(kv):
     check(o2, l2, o_ref, l_ref, tag=f"{kv} planner")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", KV_DTYPES)
 def test_attend_then_merge_equals_decode(kv):
     # The two halves of mla_decode, enqueued apart, give the same bits.
     x = make_inputs(63, [2000, 77, 900], 5, 48, kv, kv_std=0.1 if kv == "bf16" else 1.0)
@@ -154,7 +157,7 @@ def test_attend_then_merge_equals_decode(kv):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", KV_DTYPES)
 def test_dcp_shards_merge_to_full_context(kv):
     full = make_inputs(63, [1500, 700, 9, 8, 5], 5, 32, kv, kv_std=0.1 if kv == "bf16" else 1.0)
     o_full, l_full = oracle(full)
@@ -172,7 +175,7 @@ def test_dcp_shards_merge_to_full_context(kv):
     check(mo, ml, o_full, l_full, tag=f"{kv} 8-shard merge vs full context")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", KV_DTYPES)
 @pytest.mark.parametrize("W", [2, 3, 4])
 def test_other_dcp_widths_merge_to_full_context(kv, W):
     # Shard counts other than 8 (3 does not divide the page size): every
@@ -191,7 +194,7 @@ def test_other_dcp_widths_merge_to_full_context(kv, W):
     check(mo, ml, o_full, l_full, tag=f"{kv} {W}-shard merge vs full context")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", KV_DTYPES)
 def test_largest_q_len_and_many_row_groups(kv):
     # q_len 8 (the largest) x 128 heads = 1024 rows: 8 row groups per request.
     x = make_inputs(66, [700, 64, 8], 8, 128, kv, kv_std=0.1 if kv == "bf16" else 1.0)
@@ -261,3 +264,43 @@ def test_fp8_every_code_decodes_exactly():
     o = out[0, 0].double().cpu().numpy()
     want = E4M3FN_TABLE[row[:512]]
     np.testing.assert_allclose(o, np.broadcast_to(want, o.shape), rtol=1e-5, atol=0)
+
+
+def test_fp4_every_code_and_scale_decodes_exactly():
+    # One visible token and q_len 1: O is that token's c_kv, whose 16-element
+    # blocks hold every e2m1 code under block scales that span the valid
+    # range 2^-64 .. 2^64 (the dequantized BF16 value is exact, so only the
+    # fp32 division by the softmax weight rounds).  The query is zero so that
+    # the score stays 0 whatever the key: fp32 softmax arithmetic is not
+    # meant for scores near 2^64.
+    from oracle import decode_fp4_rows
+    x = make_inputs(67, [1], 1, 32, "fp4")
+    x.q_nope.zero_()
+    x.q_rope.zero_()
+    slot = int(x.req_to_token[0, 0])
+    row = np.zeros(336, dtype=np.uint8)
+    codes = np.arange(576) % 16
+    codes[16:32] = codes[16:32][::-1]
+    row[:288] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    row[288:324] = np.linspace(63, 191, 36).round().astype(np.uint8)
+    row[288 + 32:] = 127           # k_rope blocks at 2^0
+    row[288 + 33:288 + 36] = 127
+    x.pool[slot] = torch.from_numpy(row)
+    out, lse = gpu_decode(x, force_splits=1)
+    o = out[0, 0].double().cpu().numpy()
+    want = decode_fp4_rows(row[None])[0, :512]
+    np.testing.assert_allclose(o, np.broadcast_to(want, o.shape), rtol=1e-5, atol=0)
+
+
+def test_fp4_mtp_100k_workload_sampled():
+    x = config_inputs(6, device=DEV)
+    out, lse = gpu_decode(x)
+    reqs = [0, 11]
+    o_ref, l_ref = oracle(x, reqs=reqs)
+    check(out[reqs], lse[reqs], o_ref, l_ref, tag="mtp 16x100k q5 h96 fp4 (requests 0, 11)")
+
+
+def test_fp4_standard_workload_full():
+    x = config_inputs(7, device=DEV)
+    out, lse = gpu_decode(x)
+    check(out, lse, *oracle(x), tag="standard 32x4096 q1 h128 fp4 (all requests)")

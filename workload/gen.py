@@ -324,8 +324,9 @@ def shard_from_full(full: DecodeInputs, dcp_size: int, dcp_rank: int,
         dcp_size=W, dcp_rank=r, name=f"{full.name}/shard{r}", meta=dict(full.meta, shard=r))
 
 
-# The five workloads.  Each is a decode call (or, for DCP, eight shard calls
-# and one merge) on one GPU.
+# The five workloads, and two FP4-pool companions of the same shapes (6, 7).
+# Each is a decode call (or, for DCP, eight shard calls and one merge) on one
+# GPU.
 CONFIGS = {
     1: dict(name="tiny-2x1.3k-q1-h16-bf16", seq_lens=[1024, 1536], q_len=1, num_heads=16,
             kv_dtype="bf16"),
@@ -337,6 +338,10 @@ CONFIGS = {
             kv_dtype="fp8", dcp_size=8),
     5: dict(name="sweep-200k-q5-h96-fp8", seq_len=200000, q_len=5, num_heads=96,
             kv_dtype="fp8"),
+    6: dict(name="mtp-16x100k-q5-h96-fp4", seq_lens=[100000] * 16, q_len=5, num_heads=96,
+            kv_dtype="fp4"),
+    7: dict(name="standard-32x4096-q1-h128-fp4", seq_lens=[4096] * 32, q_len=1,
+            num_heads=128, kv_dtype="fp4"),
 }
 SWEEP_BATCHES = (1, 2, 4, 8, 12, 16, 20, 24)
 
