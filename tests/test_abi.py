@@ -51,13 +51,29 @@ def _desc(**kw):
 
 @pytest.mark.parametrize("bad", [dict(batch=0), dict(q_len=0), dict(q_len=9), dict(num_heads=0),
                                  dict(page_size=0), dict(dcp_size=0), dict(dcp_rank=8, dcp_size=8),
-                                 dict(dcp_rank=-1), dict(kv_dtype=7), dict(num_cus=-1),
+                                 dict(dcp_rank=-1), dict(kv_dtype=7), dict(kv_dtype=3),
+                                 dict(kv_dtype=-1), dict(num_cus=-1),
                                  dict(force_splits=-2)])
 def test_plan_rejects_invalid_descriptions(bad):
     d = _desc(**bad)
     assert mla.plan_max_bytes(d) == 0
     with pytest.raises(MlaError):
         mla.make_plan(d, [100] * max(1, d.batch))
+
+
+def test_plan_accepts_every_pool_format():
+    # BF16, FP8 and FP4 pools plan alike (the work is in tokens, not bytes).
+    plans = [mla.make_plan(_desc(kv_dtype=kv), [3000, 40]) for kv in ("bf16", "fp8", "fp4")]
+    for p, code in zip(plans, (0, 1, 2)):
+        assert p.header["kv_dtype"] == code
+    assert len({p.header["num_units"] for p in plans}) == 1
+    assert np.array_equal(plans[0].units(), plans[2].units())
+
+
+def test_fp4_format_constants_match_the_header():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    assert re.search(r"MLA_KV_FP4_E2M1\s*=\s*2", text)
+    assert "336" in text and mla._binding.FP4_ROW_BYTES == 336
 
 
 def test_plan_rejects_unsupported_dims():
