@@ -29,6 +29,9 @@ Readings where the pages are silent:
   values.
 * FP8 per-token scale = amax / 448 over the token's 576 values (1 if all are
   zero), code = e4m3fn round-to-nearest-even of x / scale, clamped to +-448.
+* FP4 rows (format and quantiser in fp4_ref): the BF16 row values are
+  quantised block by block; every step is exact (power-of-two scaling and
+  comparisons), so the stored bytes are compared bit for bit.
 
 Where floating point decides a stored code (the FP8 bytes, the BF16 bits of
 the roped values), this oracle takes each float32 step in the order the GPU
@@ -44,6 +47,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .fp4_ref import fp4_quantise_rows
 from .mla_ref import E4M3FN_TABLE, bf16_bits_to_f64
 
 D_NOPE = 128    # qk_nope_head_dim: the no-RoPE query width before absorption
@@ -158,9 +162,10 @@ def kv_append_ref(pool, kv_scale, c_kv_bits, k_rope_bits, cos_sin, positions, sl
                   kv_dtype: str):
     """Pool (and scales) after appending the T new rows at `slots`.
 
-    pool: uint16 BF16 bits [num_slots, 576] or uint8 e4m3fn codes; kv_scale:
-    float32 [num_slots] (FP8) or None.  Slots outside [0, num_slots) are
-    skipped (a token another DCP shard holds); the others must be distinct.
+    pool: uint16 BF16 bits [num_slots, 576], uint8 e4m3fn codes, or uint8 FP4
+    rows [num_slots, 336]; kv_scale: float32 [num_slots] (FP8) or None.
+    Slots outside [0, num_slots) are skipped (a token another DCP shard
+    holds); the others must be distinct.
     Returns new arrays; the inputs are not modified.
     """
     rows = latent_rows_ref(c_kv_bits, k_rope_bits, cos_sin, positions)
@@ -169,6 +174,9 @@ def kv_append_ref(pool, kv_scale, c_kv_bits, k_rope_bits, cos_sin, positions, sl
     keep = (sl >= 0) & (sl < pool.shape[0])
     if kv_dtype == "bf16":
         pool[sl[keep]] = rows[keep]
+        return pool, None
+    if kv_dtype == "fp4":
+        pool[sl[keep]] = fp4_quantise_rows(bf16_bits_to_f32(rows[keep]))
         return pool, None
     if kv_dtype != "fp8":
         raise ValueError(f"unknown kv_dtype {kv_dtype!r}")

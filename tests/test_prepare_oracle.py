@@ -194,6 +194,9 @@ def _append_case(kv, seed=8, T=6, n=20):
     if kv == "bf16":
         pool = _bf16_bits(rng, (n, 576))
         sc = None
+    elif kv == "fp4":
+        pool = rng.integers(0, 255, (n, 336)).astype(np.uint8)
+        sc = None
     else:
         pool = rng.integers(0, 255, (n, 576)).astype(np.uint8)
         sc = rng.uniform(0.01, 0.05, n).astype(np.float32)
@@ -231,6 +234,29 @@ def test_fp8_append_scale_codes_and_error():
     untouched = np.setdiff1d(np.arange(len(pool)), slots[slots >= 0])
     np.testing.assert_array_equal(new[untouched], pool[untouched])
     np.testing.assert_array_equal(nsc[untouched], sc[untouched])
+
+
+def test_fp4_append_writes_rows_within_half_a_grid_step():
+    # FP4 rows of the roped latent rows: within half of the e2m1 grid gap
+    # (at most 2^e, between the codes 4 and 6) of every value, each block's
+    # exponent the smallest that holds its largest value, the padding zero;
+    # other slots untouched.
+    c_kv, k_rope, tab, pos, slots, pool, _ = _append_case("fp4")
+    new, nsc = P.kv_append_ref(pool, None, c_kv, k_rope, tab, pos, slots, "fp4")
+    assert nsc is None
+    rows = P.bf16_bits_to_f32(P.latent_rows_ref(c_kv, k_rope, tab, pos)).astype(np.float64)
+    for t, sl in enumerate(slots):
+        if sl < 0:
+            continue
+        dec = oracle.decode_fp4_rows(new[sl][None])[0]
+        e = new[sl, 288:324].astype(np.int64) - 127
+        step = np.repeat(np.ldexp(1.0, e), 16)
+        assert np.all(np.abs(dec - rows[t]) <= step)
+        amax = np.abs(rows[t]).reshape(36, 16).max(axis=1)
+        assert np.all(amax <= 6.0 * np.ldexp(1.0, e)) and np.all(amax > 3.0 * np.ldexp(1.0, e))
+        assert not new[sl, 324:].any()
+    untouched = np.setdiff1d(np.arange(len(pool)), slots[slots >= 0])
+    np.testing.assert_array_equal(new[untouched], pool[untouched])
 
 
 def test_fp8_append_zero_row():
