@@ -125,11 +125,12 @@ def algorithmic_counts(x):
 def prepare_bytes(x) -> float:
     """Algorithmic HBM bytes of one mla_prepare call: w_kc read once, the
     queries read and written once, the new rows and their positions' cos /
-    sin read once, and the pool rows (and FP8 scales) written once."""
+    sin read once, and the pool rows (and FP8 scales) written once (FP4: 336
+    bytes a row)."""
     T, H = x["T"], x["H"]
-    e = 1 if x["kv_dtype"] == "fp8" else 2
+    row = {"bf16": 576 * 2, "fp8": 576 + 4, "fp4": 336}[x["kv_dtype"]]
     return float(H * 512 * 128 * 2 + T * H * 128 * 2 + 2 * T * H * 64 * 2 + T * H * 512 * 2
-                 + T * 576 * 2 + T * 64 * 4 + T * (576 * e + (4 if e == 1 else 0)) + T * 8)
+                 + T * 576 * 2 + T * 64 * 4 + T * row + T * 8)
 
 
 def run_prepare(args, dev):

@@ -120,7 +120,8 @@ mla_status mla_prepare(int32_t num_tokens, int32_t num_heads, int32_t kv_dtype,
                        void* q_nope_absorbed, void* q_rope_out, void* kv_pool, float* kv_scale,
                        int64_t num_slots, void* stream) {
   if (num_tokens < 0 || num_heads < 1 || max_pos < 1 || num_slots < 1) return MLA_ERR_INVALID_ARG;
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARG;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_FP4_E2M1)
+    return MLA_ERR_INVALID_ARG;
   const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
   for (const void* p : {q_nope, q_rope_in, w_kc_t, c_kv_new, k_rope_new, (const void*)positions,
                         (const void*)cos_sin, (const void*)slots, (const void*)q_nope_absorbed,
@@ -133,7 +134,7 @@ mla_status mla_prepare(int32_t num_tokens, int32_t num_heads, int32_t kv_dtype,
   a.T = num_tokens;
   a.H = num_heads;
   a.max_pos = max_pos;
-  a.fp8 = fp8;
+  a.kv = kv_dtype;
   a.num_slots = num_slots;
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_rope_in = static_cast<const uint16_t*>(q_rope_in);

@@ -10,8 +10,10 @@
 // RoPE and append  RoPE of every head's q_rope and of the new tokens'
 //                   k_rope (interleaved pairs, caller-given cos / sin), then
 //                   the append of the rows [c_kv | roped k_rope] to the pool
-//                   at the given slots: BF16 bits, or e4m3fn codes with the
-//                   per-token scale amax / 448.
+//                   at the given slots: BF16 bits, e4m3fn codes with the
+//                   per-token scale amax / 448, or FP4 rows (e2m1 codes with
+//                   a power-of-two scale per 16 elements; page "resident
+//                   VRAM accounting", sections "KV ledger" and "cell_size").
 //
 // Every float32 step that decides a stored bit (the roped values, the scale,
 // the quotients) is a correctly rounded IEEE operation with no contraction,
@@ -133,6 +135,66 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 
+// FP4 row of one token: thread i holds elements 2 i, 2 i + 1 of c_kv (c0,
+// c1) and threads 0..31 also elements 512 + 2 i, + 1 of the roped k_rope (r0,
+// r1).  Block k (16 elements) lies in threads 8 k .. 8 k + 7 (c_kv blocks 0..31;
+// k_rope blocks 32..35 in threads 8 (k - 32) ..), so its largest magnitude
+// is a reduction over 8 neighbouring lanes.  Its exponent e is the smallest
+// with amax <= 6 * 2^e: with amax = f 2^E (0.5 <= f < 1), e = E - 3 if f <=
+// 0.75, else E - 2; clamped to [-64, 64] (amax below 2^-100 takes -64, which
+// is what the rule gives there).  Codes: e2m1 nearest to x 2^-e, ties to the
+// even code, found by exact comparisons with the midpoints of the grid.
+__device__ __forceinline__ int fp4_block_exponent(float amax) {
+  if (!(amax >= 0x1p-100f)) return -64;
+  const float f = __builtin_amdgcn_frexp_mantf(amax);
+  const int E = __builtin_amdgcn_frexp_expf(amax);
+  const int e = f <= 0.75f ? E - 3 : E - 2;
+  return e > 64 ? 64 : (e < -64 ? -64 : e);
+}
+
+__device__ __forceinline__ uint32_t e2m1_code(float x, int e) {
+  const float y = __builtin_amdgcn_ldexpf(x, -e);   // exact (power-of-two scaling)
+  const float a = fabsf(y);
+  const uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                     (a >= 3.5f) + (a > 5.0f);
+  return m | ((__builtin_bit_cast(uint32_t, y) >> 28) & 0x8u);
+}
+
+__device__ __forceinline__ float max8(float v) {
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Four bytes of lanes i .. i + 3 (gathered by lane i) and of lanes i, i + 8,
+// i + 16, i + 24.
+__device__ __forceinline__ uint32_t gather4(uint32_t b, int stride) {
+  return b | (__shfl_down(b, stride) << 8) | (__shfl_down(b, 2 * stride) << 16) |
+         (__shfl_down(b, 3 * stride) << 24);
+}
+
+__device__ __forceinline__ void append_fp4(uint8_t* row, int tid, float c0, float c1, float r0,
+                                           float r1) {
+  const int ec = fp4_block_exponent(max8(fmaxf(fabsf(c0), fabsf(c1))));
+  const uint32_t bc = e2m1_code(c0, ec) | (e2m1_code(c1, ec) << 4);
+  // The k_rope reduction runs in all of wave 0 (lanes 32..63 hold zeros).
+  const int er = fp4_block_exponent(max8(fmaxf(fabsf(r0), fabsf(r1))));
+  const uint32_t br = e2m1_code(r0, er) | (e2m1_code(r1, er) << 4);
+  uint32_t* row32 = reinterpret_cast<uint32_t*>(row);
+  const uint32_t codes = gather4(bc, 1);
+  const uint32_t scales = gather4((uint32_t)(ec + 127), 8);
+  const uint32_t rcodes = gather4(br, 1);
+  const uint32_t rscales = gather4((uint32_t)(er + 127), 8);
+  if ((tid & 3) == 0) row32[tid >> 2] = codes;                    // bytes 0..255
+  if ((tid & 31) == 0) row32[72 + (tid >> 5)] = scales;          // bytes 288..319
+  if (tid < 32) {
+    if ((tid & 3) == 0) row32[64 + (tid >> 2)] = rcodes;          // bytes 256..287
+    if (tid == 0) row32[80] = rscales;                            // bytes 320..323
+  } else if (tid < 35) {
+    row32[81 + (tid - 32)] = 0u;                                  // padding 324..335
+  }
+}
+
 // One block per new token.  Threads 0..255 rotate the token's q_rope pairs
 // (H x 32 of them), then thread i takes c_kv elements 2 i, 2 i + 1 and
 // threads 0..31 the k_rope pair i of the row to append.
@@ -159,7 +221,13 @@ __device__ __forceinline__ void rope_append_block(const PrepareArgs& a, int t, f
     const uint32_t kin = reinterpret_cast<const uint32_t*>(a.k_rope_new + (int64_t)t * 64)[tid];
     kr = rope_pair(kin, c, s);
   }
-  if (!a.fp8) {
+  if (a.kv == 2) {
+    const float r0 = tid < 32 ? bf16_lo(kr) : 0.f, r1 = tid < 32 ? bf16_hi(kr) : 0.f;
+    append_fp4(static_cast<uint8_t*>(a.pool) + slot * 336, tid, bf16_lo(ckv), bf16_hi(ckv), r0,
+               r1);
+    return;
+  }
+  if (a.kv == 0) {
     uint32_t* row = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.pool) + slot * 576);
     row[tid] = ckv;
     if (tid < 32) row[256 + tid] = kr;

@@ -179,7 +179,8 @@ def test_prepare_rejects_bad_arguments_on_host():
     assert call(T=0, kv=0, scale=None) == 0
     assert call(T=-1) == -1
     assert call(H=0) == -1
-    assert call(kv=2) == -1
+    assert call(kv=3) == -1                          # not a pool format (2 is FP4)
+    assert call(kv=-1) == -1
     assert call(max_pos=0) == -1
     assert call(nslots=0) == -1
     assert call(ptrs=[None, f, f, f, f]) == -1

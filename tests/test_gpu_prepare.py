@@ -2,10 +2,11 @@
 
 The absorbed query is a float32-accumulated sum rounded to BF16: each element
 must lie within one BF16 unit in the last place of the float64 reference.
-The roped query, the appended pool rows (BF16 bits or e4m3fn codes) and the
-FP8 scales are bytes decided by correctly rounded float32 steps that the
-oracle repeats in the same order, so they must match bit for bit, and every
-slot the call does not store must be left as it was.
+The roped query, the appended pool rows (BF16 bits, e4m3fn codes or FP4
+rows) and the FP8 scales are bytes decided by correctly rounded float32
+steps that the oracle repeats in the same order (FP4: power-of-two scaling
+and comparisons, exact on both sides), so they must match bit for bit, and
+every slot the call does not store must be left as it was.
 """
 
 import numpy as np
@@ -44,6 +45,9 @@ def _case(seed, T, H, kv, num_slots=None, max_pos=4096, skip=True):
     x["slots"] = torch.from_numpy(slots)
     if kv == "bf16":
         x["kv_pool"] = bf16((num_slots, 576), 1.0)
+        x["kv_scale"] = None
+    elif kv == "fp4":
+        x["kv_pool"] = torch.from_numpy(rng.integers(0, 256, (num_slots, 336)).astype(np.uint8))
         x["kv_scale"] = None
     else:
         x["kv_pool"] = torch.from_numpy(rng.integers(0, 0x7E, (num_slots, 576)).astype(np.uint8))
@@ -84,17 +88,18 @@ def _check(x, kv, tag):
         np.testing.assert_array_equal(_bits(pool), pool_ref, err_msg=f"{tag}: pool")
     else:
         np.testing.assert_array_equal(pool.cpu().numpy(), pool_ref, err_msg=f"{tag}: pool codes")
+    if sc_ref is not None:
         np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), sc_ref.view(np.uint32),
                                       err_msg=f"{tag}: scales")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4"])
 @pytest.mark.parametrize("T,H", [(80, 96), (37, 128), (1, 16), (640, 96), (33, 1)])
 def test_prepare_matches_oracle(kv, T, H):
     _check(_case(10 * T + H, T, H, kv), kv, f"{kv} T{T} H{H}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4"])
 def test_prepare_edge_inputs(kv):
     x = _case(5, 12, 8, kv, max_pos=64)
     pos = x["positions"].numpy()
@@ -109,3 +114,25 @@ def test_prepare_edge_inputs(kv):
     k[5, :] = 300.0                                    # one token dominated by its RoPE part
     x["k_rope_new"] = torch.from_numpy(k).to(torch.bfloat16)
     _check(x, kv, f"{kv} edge inputs")
+
+
+def test_prepare_fp4_block_edges():
+    # FP4 blocks whose largest value sits exactly on 6 * 2^e and just above
+    # it, elements on the midpoints of the e2m1 grid (ties to the even code)
+    # and just off them, a block of zeros and tiny values, and a huge block.
+    x = _case(6, 8, 4, "fp4")
+    c = np.zeros((8, 512), np.float32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    for t in range(8):
+        e = t - 4
+        c[t, 0] = 6.0 * 2.0 ** e
+        c[t, 1:8] = mids * 2.0 ** e
+        c[t, 8:15] = -mids * 2.0 ** e
+        # one BF16 unit in the last place above (the inputs are BF16)
+        c[t, 16] = (6.0 + 2.0 ** -5) * 2.0 ** e
+        c[t, 17:24] = (mids + np.exp2(np.floor(np.log2(mids)) - 7)) * 2.0 ** e
+        c[t, 48:64] = 1e-30
+        c[t, 64:80] = 3e38 if t == 0 else 1.0
+        c[t, 80:] = np.random.default_rng(t).standard_normal(432) * 2.0 ** e
+    x["c_kv_new"] = torch.from_numpy(c).to(torch.bfloat16)
+    _check(x, "fp4", "fp4 block edges")

@@ -372,6 +372,7 @@ PREPARE_CONFIGS = {
     "mtp": dict(name="prepare-mtp-80x96-fp8", T=16 * 5, H=96, kv_dtype="fp8"),
     "dcp8": dict(name="prepare-dcp8-640x96-fp8", T=128 * 5, H=96, kv_dtype="fp8"),
     "standard": dict(name="prepare-standard-32x128-bf16", T=32, H=128, kv_dtype="bf16"),
+    "mtp-fp4": dict(name="prepare-mtp-80x96-fp4", T=16 * 5, H=96, kv_dtype="fp4"),
 }
 
 
@@ -393,6 +394,9 @@ def prepare_inputs(key: str, device="cpu", num_slots: int = 1 << 18, max_pos: in
     x["slots"] = torch.from_numpy(rng.permutation(num_slots)[:T].astype(np.int32))
     if kv == "bf16":
         x["kv_pool"] = torch.zeros((num_slots, 576), dtype=torch.bfloat16)
+        x["kv_scale"] = None
+    elif kv == "fp4":
+        x["kv_pool"] = torch.zeros((num_slots, FP4_ROW_BYTES), dtype=torch.uint8)
         x["kv_scale"] = None
     else:
         x["kv_pool"] = torch.zeros((num_slots, 576), dtype=torch.uint8)
