@@ -1,0 +1,81 @@
+"""GPU: the prepare step feeding decode, against the oracle's same chain.
+
+The q_len new tokens of every request are appended by mla_prepare at their
+pool slots (the last q positions of the request), with their absorbed and
+roped queries; mla_decode then attends over the pool, the new rows included.
+The oracle runs the same two steps from the same inputs (its absorbed query
+rounded to BF16, nearest-even), so nothing the GPU computed feeds it.  The
+decode tolerance applies (max |dO| <= 2e-2, relative 1e-2, |dLSE| <= 1e-3).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_absorbed_amd as mla
+from oracle import mla_decode_ref
+from oracle import prepare_ref as P
+from workload import make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4"])
+def test_prepare_then_decode(kv):
+    q, H = 5, 16
+    x = make_inputs(71, [300, 97, 5], q, H, kv, kv_std=0.1 if kv == "bf16" else 1.0)
+    B = x.batch
+    rng = np.random.default_rng(np.random.SeedSequence([72, ord(kv[-1])]))
+
+    def bf16(shape, std):
+        return torch.from_numpy((rng.standard_normal(shape) * std).astype(np.float32)).to(
+            torch.bfloat16)
+    T = B * q
+    max_pos = 512
+    table = x.req_to_token.cpu().numpy()
+    pos = np.array([int(L) - q + i for L in x.seq_lens for i in range(q)], np.int32)
+    slots = np.array([table[b, int(x.seq_lens[b]) - q + i] for b in range(B) for i in range(q)],
+                     np.int32)
+    ins = dict(q_nope=bf16((T, H, 128), 1.0), q_rope_in=bf16((T, H, 64), 0.1),
+               w_kc_t=bf16((H, 512, 128), 0.01), c_kv_new=bf16((T, 512), 0.1),
+               k_rope_new=bf16((T, 64), 0.1), positions=torch.from_numpy(pos),
+               slots=torch.from_numpy(slots))
+    ang = np.arange(max_pos)[:, None] * (10000.0 ** (-np.arange(32) / 32.0))[None, :]
+    ins["cos_sin"] = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(
+        np.float32))
+
+    # ---- oracle chain
+    nb = x.numpy_bits()
+    qa_ref, qr_ref, pool_ref, sc_ref = P.mla_prepare_ref(
+        _bits(ins["q_nope"]), _bits(ins["q_rope_in"]), _bits(ins["w_kc_t"]),
+        _bits(ins["c_kv_new"]), _bits(ins["k_rope_new"]), ins["cos_sin"].numpy(), pos, slots,
+        nb["pool"], nb["kv_scale"], kv)
+    qa_bits = P.f32_to_bf16_bits(qa_ref.astype(np.float32)).reshape(B, q, H, 512)
+    o_ref, l_ref = mla_decode_ref(qa_bits, qr_ref.reshape(B, q, H, 64), pool_ref, sc_ref,
+                                  nb["req_to_token"], nb["seq_lens"], q, x.softmax_scale, kv)
+
+    # ---- GPU chain
+    g = {k: v.to(DEV) for k, v in ins.items()}
+    gx = x.to(DEV)
+    qa, qr = mla.prepare(g["q_nope"], g["q_rope_in"], g["w_kc_t"], g["c_kv_new"],
+                         g["k_rope_new"], g["positions"], g["cos_sin"], g["slots"], gx.pool,
+                         gx.kv_scale)
+    plan = mla.make_plan(mla.make_desc(B, q, H, kv, page_size=x.page_size), x.seq_lens,
+                         device=DEV)
+    out, lse = mla.decode(plan, qa.view(B, q, H, 512), qr.view(B, q, H, 64), gx.pool,
+                          gx.kv_scale, gx.req_to_token,
+                          torch.from_numpy(np.asarray(x.seq_lens, np.int32)).to(DEV),
+                          x.softmax_scale)
+    torch.cuda.synchronize()
+    o = out.double().cpu().numpy()
+    l = lse.double().cpu().numpy()
+    err_o = np.abs(o - o_ref).max()
+    rel = np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref)
+    err_l = np.abs(l - l_ref).max()
+    print(f"[pipeline] {kv}: max|dO|={err_o:.3e} rel={rel:.3e} max|dLSE|={err_l:.3e}", flush=True)
+    assert err_o <= 2e-2 and rel <= 1e-2 and err_l <= 1e-3
