@@ -16,6 +16,7 @@ Statements (T = BF16 or FP8):
   MLA_QK_T_ASM       QK (first tile of a unit)
   MLA_FUSED_BF16_ASM QK of tile t+1 and PV of tile t, plus DMA
   MLA_FUSED_BF16_NODMA_ASM  the same without the DMA (FP4 pools)
+  MLA_FUSED_BF16_DQ_ASM  the same plus the dequantization of a raw FP4 tile
   MLA_PV_T_ASM       PV (last tile of a unit)
   FP8, pipelined one tile deeper so that the softmax runs in the MFMA shadow:
   MLA_QKSM_FP8_ASM   QK of tile t+1 and SM of tile t, plus DMA (first step)
@@ -319,8 +320,91 @@ def sm_program(fp8: bool, sk: int, tmp: int):
     return prog
 
 
+FP4_SEL = ("", " op_sel:[1,0,0]", " op_sel:[0,1,0]", " op_sel:[1,1,0]")  # byte 0..3
+
+
+def dq_program(base: int):
+    """Dequantization of one raw FP4 tile into the BF16 tile layout, as a list
+    of (kind, text, reads, writes, tag) like the softmax program, for the
+    statement to spread over its MFMA slots.
+
+    Raw tile: code chunk c (16 bytes: blocks 2 c and 2 c + 1) of token t at
+    512 c + 16 t; the scale byte of block b of token t at 512 (18 + b / 16) +
+    16 t + b % 16.  BF16 tile: chunk cc of token t at 512 cc + 16 (t ^ 4 (cc
+    & 3)).  Lane (t, h) = (lane % 32, lane / 32) of wave w converts the code
+    chunks c = 2 w + h and 2 w + h + 8 whole (blocks in halves of 8 bytes),
+    and one dword (chunk w) of code chunk 16 + h: every wave 2.25 chunks.
+    The lane terms (16 t, and 32 h from which 512 h, 2 h and 2048 h follow)
+    are computed here from the lane id; the wave terms come in scalars:
+    %[dqa] = raw + 1024 w, %[dqb] = raw + 4 w, %[dqc] = bf16 tile + 4096 w,
+    %[dqd] = raw + w / 2, %[dqe] = 64 w, %[dqf] = bf16 tile + 512 w.
+    Scratch: codes (2), one BF16 pair (2), scale, two addresses, 16 t, 32 h.
+    """
+    # nine registers from an odd base, so that the two pairs start on even
+    # registers (as the ISA requires)
+    assert base % 2 == 1
+    SC, C, O, T, T2, TT, HH = base, base + 1, base + 3, base + 5, base + 6, base + 7, base + 8
+    prog = []
+
+    def valu(text):
+        prog.append(("valu", text, [], [], None))
+
+    def lds(text, tag):
+        prog.append(("lds", text, [], [], tag))
+
+    def wait(tag):
+        prog.append(("wait", "", [], [], tag))
+
+    def convert_dword(src, write_addr, off):
+        # 8 codes of one dword -> one 16-byte BF16 chunk, written in halves
+        for q2 in (0, 1):
+            for b in (0, 1):
+                valu(f"v_cvt_scalef32_pk_bf16_fp4 v{O + b}, v{src}, v{SC}{FP4_SEL[2 * q2 + b]}")
+            lds(f"ds_write_b64 {write_addr}, v[{O}:{O + 1}] offset:{off + 8 * q2}", ("DQW",))
+
+    valu(f"v_mbcnt_lo_u32_b32 v{TT}, -1, 0")
+    valu(f"v_mbcnt_hi_u32_b32 v{TT}, -1, v{TT}")
+    valu(f"v_and_b32 v{HH}, 32, v{TT}")                 # 32 h
+    valu(f"v_and_b32 v{TT}, 31, v{TT}")
+    valu(f"v_lshlrev_b32 v{TT}, 4, v{TT}")              # 16 t
+    for k in (0, 1):
+        for hh in (0, 1):
+            tag = ("DQ", k, hh)
+            valu(f"v_lshl_add_u32 v{T}, v{HH}, 4, v{TT}")           # 16 t + 512 h
+            valu(f"v_add_u32 v{T}, %[dqa], v{T}")
+            lds(f"ds_read_b64 v[{C}:{C + 1}], v{T} offset:{4096 * k + 8 * hh}", tag + ("c",))
+            valu(f"v_lshrrev_b32 v{T}, 4, v{HH}")                   # 2 h
+            valu(f"v_add3_u32 v{T}, %[dqb], v{T}, v{TT}")
+            lds(f"ds_read_u8 v{SC}, v{T} offset:{9216 + 512 * k + hh}", tag + ("s",))
+            wait(tag + ("s",))
+            valu(f"v_lshlrev_b32 v{SC}, 23, v{SC}")
+            wait(tag + ("c",))
+            for jj in (0, 1):
+                j = 2 * hh + jj
+                valu(f"v_xor_b32 v{T2}, {64 * j}, v{TT}")
+                valu(f"v_lshl_add_u32 v{T2}, v{HH}, 6, v{T2}")        # + 2048 h
+                valu(f"v_add_u32 v{T2}, %[dqc], v{T2}")
+                convert_dword(C + jj, f"v{T2}", 16384 * k + 512 * j)
+    # The 64 units of code chunks 16, 17: wave w takes their dword w.
+    tag = ("DQ", 2)
+    valu(f"v_lshl_add_u32 v{T}, v{HH}, 4, v{TT}")
+    valu(f"v_add_u32 v{T}, %[dqb], v{T}")
+    lds(f"ds_read_b32 v{C}, v{T} offset:8192", tag + ("c",))
+    valu(f"v_lshrrev_b32 v{T}, 4, v{HH}")
+    valu(f"v_add3_u32 v{T}, %[dqd], v{T}, v{TT}")
+    lds(f"ds_read_u8 v{SC}, v{T} offset:10240", tag + ("s",))
+    wait(tag + ("s",))
+    valu(f"v_lshlrev_b32 v{SC}, 23, v{SC}")
+    wait(tag + ("c",))
+    valu(f"v_xor_b32 v{T2}, %[dqe], v{TT}")
+    valu(f"v_lshl_add_u32 v{T2}, v{HH}, 6, v{T2}")
+    valu(f"v_add_u32 v{T2}, %[dqf], v{T2}")
+    convert_dword(C, f"v{T2}", 32768)
+    return prog
+
+
 def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
-              tail_chains: int = 2):
+              tail_chains: int = 2, dq: bool = False):
     reads = {}
     kops, vops = [], []
     if qk:
@@ -417,12 +501,16 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
     if sm:
         rings["SK"] = (1, 4)
         rings["ST"] = (1, 4)
+    if dq:
+        rings["DQ"] = (1, 9)
     st = Stream(rings)
     st.emit("s_nop 2")  # operands may have just been written by VALU instructions
     if n_dma:
         st.emit("s_mov_b32 %[m0s], m0")  # M0 is handed back unchanged
 
     smp = sm_program(fp8, st.base["SK"], st.base["ST"]) if sm else []
+    if dq:
+        smp = smp + dq_program(st.base["DQ"])
     sm_next = [0]
 
     queue = {}
@@ -654,8 +742,10 @@ STATEMENTS = (
     ("MLA_SM_FP8_ASM", dict(fp8=True, qk=False, pv=False, sm=True)),
     ("MLA_PV_FP8_ASM", dict(fp8=True, qk=False, pv=True)),
     # FP4 pools: the BF16 tiles are dequantized in LDS, and the FP4 DMA is
-    # issued outside the statement.
+    # issued outside the statement; the steady state dequantizes the tile
+    # after next inside the statement.
     ("MLA_FUSED_BF16_NODMA_ASM", dict(fp8=False, qk=True, pv=True)),
+    ("MLA_FUSED_BF16_DQ_ASM", dict(fp8=False, qk=True, pv=True, dq=True)),
 )
 
 
