@@ -30,10 +30,12 @@ they are silent are listed in the module docstring of ``mla_ref``.
 
 ``fp4_ref`` defines the FP4 KV rows (e2m1 codes with one power-of-two
 scale per 16 elements; VRAM page, "KV ledger" and "cell_size" sections) and
-their quantiser.  ``prepare_ref`` is the oracle of the step before
-attention (Q absorption, RoPE, KV append), ``project_ref`` that of the step
-after it (the LSE merge followed by the w_vc up-projection); their readings
-are in their own module docstrings.
+their quantiser; ``mxfp8_ref`` the MXFP8 rows (e4m3fn codes with one
+power-of-two scale per 32 elements; "cell_size" section).  ``prepare_ref``
+is the oracle of the step before attention (Q absorption, RoPE, KV
+append), ``project_ref`` that of the step after it (the LSE merge followed
+by the w_vc up-projection); their readings are in their own module
+docstrings.
 """
 
 from .mla_ref import (  # noqa: F401
@@ -73,6 +75,10 @@ from .fp4_ref import (  # noqa: F401
     decode_fp4_rows,
     block_exponent_of,
     fp4_quantise_rows,
+)
+from .mxfp8_ref import (  # noqa: F401
+    decode_mxfp8_rows,
+    mxfp8_quantise_rows,
 )
 from .project_ref import (  # noqa: F401
     vc_project_ref,

@@ -12,8 +12,9 @@ What is computed, for request b, draft position i in [0, q) and head h:
    tokens; section "problem: how to split" for slot p -> rank p % 8.)
 2. Keys.  slot = req_to_token[b, j]; the key is the whole 576-wide latent row
    [c_kv (512) | k_rope (64)] of that slot, decoded exactly to float64: BF16
-   bits, OCP e4m3fn codes times the slot's fp32 scale, or FP4 codes times
-   their block scale (format and readings in fp4_ref).  (VRAM page,
+   bits, OCP e4m3fn codes times the slot's fp32 scale, or FP4 / MXFP8
+   codes times their block scale (formats and readings in fp4_ref and
+   mxfp8_ref).  (VRAM page,
    "KV ledger" MLA bullet and the "cell_size" MLA pool shape
    (size + page_size, 1, kv_lora_rank + qk_rope_head_dim).)
 3. Values.  The first 512 elements of the same row (the latent c_kv).
@@ -117,6 +118,9 @@ def dequant_rows(pool: np.ndarray, kv_scale, slots: np.ndarray,
         return E4M3FN_TABLE[raw.astype(np.intp)] * scale[:, None]
     if kv_dtype == "fp4":
         return decode_fp4_rows(raw)
+    if kv_dtype == "mxfp8":
+        from .mxfp8_ref import decode_mxfp8_rows   # (it imports this module)
+        return decode_mxfp8_rows(raw)
     raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
 
 
@@ -157,8 +161,9 @@ def mla_decode_ref(q_nope, q_rope, pool, kv_scale, req_to_token, seq_lens,
     Arguments are the stored bit patterns, as numpy arrays:
       q_nope        uint16 [B, q, H, 512]  BF16 bits of the absorbed no-RoPE query
       q_rope        uint16 [B, q, H, 64]   BF16 bits of the RoPE query
-      pool          uint16 [S, 576] (BF16 bits), uint8 [S, 576] (e4m3fn codes) or
-                    uint8 [S, 336] (FP4 rows, format in fp4_ref)
+      pool          uint16 [S, 576] (BF16 bits), uint8 [S, 576] (e4m3fn codes),
+                    uint8 [S, 336] (FP4 rows, format in fp4_ref) or uint8
+                    [S, 608] (MXFP8 rows, format in mxfp8_ref)
       kv_scale      float32 [S] for FP8, ignored otherwise
       req_to_token  int32 [B, >= local length]; column j is local index j
       seq_lens      int [B]; global lengths L_b including the q drafts

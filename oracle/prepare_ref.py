@@ -29,9 +29,10 @@ Readings where the pages are silent:
   values.
 * FP8 per-token scale = amax / 448 over the token's 576 values (1 if all are
   zero), code = e4m3fn round-to-nearest-even of x / scale, clamped to +-448.
-* FP4 rows (format and quantiser in fp4_ref): the BF16 row values are
-  quantised block by block; every step is exact (power-of-two scaling and
-  comparisons), so the stored bytes are compared bit for bit.
+* FP4 and MXFP8 rows (formats and quantisers in fp4_ref and mxfp8_ref):
+  the BF16 row values are quantised block by block; every step is exact
+  (power-of-two scaling, comparisons, one nearest-even rounding of an exact
+  value), so the stored bytes are compared bit for bit.
 
 Where floating point decides a stored code (the FP8 bytes, the BF16 bits of
 the roped values), this oracle takes each float32 step in the order the GPU
@@ -48,6 +49,7 @@ from __future__ import annotations
 import numpy as np
 
 from .fp4_ref import fp4_quantise_rows
+from .mxfp8_ref import mxfp8_quantise_rows
 from .mla_ref import E4M3FN_TABLE, bf16_bits_to_f64
 
 D_NOPE = 128    # qk_nope_head_dim: the no-RoPE query width before absorption
@@ -162,8 +164,9 @@ def kv_append_ref(pool, kv_scale, c_kv_bits, k_rope_bits, cos_sin, positions, sl
                   kv_dtype: str):
     """Pool (and scales) after appending the T new rows at `slots`.
 
-    pool: uint16 BF16 bits [num_slots, 576], uint8 e4m3fn codes, or uint8 FP4
-    rows [num_slots, 336]; kv_scale: float32 [num_slots] (FP8) or None.
+    pool: uint16 BF16 bits [num_slots, 576], uint8 e4m3fn codes, uint8 FP4
+    rows [num_slots, 336] or MXFP8 rows [num_slots, 608]; kv_scale: float32
+    [num_slots] (FP8) or None.
     Slots outside [0, num_slots) are skipped (a token another DCP shard
     holds); the others must be distinct.
     Returns new arrays; the inputs are not modified.
@@ -177,6 +180,9 @@ def kv_append_ref(pool, kv_scale, c_kv_bits, k_rope_bits, cos_sin, positions, sl
         return pool, None
     if kv_dtype == "fp4":
         pool[sl[keep]] = fp4_quantise_rows(bf16_bits_to_f32(rows[keep]))
+        return pool, None
+    if kv_dtype == "mxfp8":
+        pool[sl[keep]] = mxfp8_quantise_rows(bf16_bits_to_f32(rows[keep]))
         return pool, None
     if kv_dtype != "fp8":
         raise ValueError(f"unknown kv_dtype {kv_dtype!r}")

@@ -197,6 +197,9 @@ def _append_case(kv, seed=8, T=6, n=20):
     elif kv == "fp4":
         pool = rng.integers(0, 255, (n, 336)).astype(np.uint8)
         sc = None
+    elif kv == "mxfp8":
+        pool = rng.integers(0, 255, (n, 608)).astype(np.uint8)
+        sc = None
     else:
         pool = rng.integers(0, 255, (n, 576)).astype(np.uint8)
         sc = rng.uniform(0.01, 0.05, n).astype(np.float32)
@@ -255,6 +258,29 @@ def test_fp4_append_writes_rows_within_half_a_grid_step():
         amax = np.abs(rows[t]).reshape(36, 16).max(axis=1)
         assert np.all(amax <= 6.0 * np.ldexp(1.0, e)) and np.all(amax > 3.0 * np.ldexp(1.0, e))
         assert not new[sl, 324:].any()
+    untouched = np.setdiff1d(np.arange(len(pool)), slots[slots >= 0])
+    np.testing.assert_array_equal(new[untouched], pool[untouched])
+
+
+def test_mxfp8_append_writes_rows_within_half_a_step():
+    # MXFP8 rows: within half an e4m3 step of every value (2^-4 relative,
+    # 2^-10 * 2^e below the normal range), each block's exponent the
+    # smallest that holds its largest value, the padding zero.
+    c_kv, k_rope, tab, pos, slots, pool, _ = _append_case("mxfp8")
+    new, nsc = P.kv_append_ref(pool, None, c_kv, k_rope, tab, pos, slots, "mxfp8")
+    assert nsc is None
+    rows = P.bf16_bits_to_f32(P.latent_rows_ref(c_kv, k_rope, tab, pos)).astype(np.float64)
+    for t, sl in enumerate(slots):
+        if sl < 0:
+            continue
+        dec = oracle.decode_mxfp8_rows(new[sl][None])[0]
+        e = new[sl, 576:594].astype(np.int64) - 127
+        sc = np.repeat(np.ldexp(1.0, e), 32)
+        bound = np.maximum(np.abs(rows[t]) * 2.0 ** -4, 2.0 ** -10 * sc) * 1.0001
+        assert np.all(np.abs(dec - rows[t]) <= bound)
+        amax = np.abs(rows[t]).reshape(18, 32).max(axis=1)
+        assert np.all(amax <= 448.0 * np.ldexp(1.0, e)) and np.all(amax > 224.0 * np.ldexp(1.0, e))
+        assert not new[sl, 594:].any()
     untouched = np.setdiff1d(np.arange(len(pool)), slots[slots >= 0])
     np.testing.assert_array_equal(new[untouched], pool[untouched])
 

@@ -41,6 +41,9 @@ FP4_ROW_BYTES = 336
 FP4_CODE_BYTES = 288
 FP4_POISON_CODES = 0x77     # e2m1 6.0 in both nibbles
 FP4_POISON_SCALE = 0xFF     # not a valid scale code
+# MXFP8 rows: 576 e4m3fn codes, 18 block-scale bytes (one per 32 elements,
+# bias 127), 14 bytes of zero padding.
+MXFP8_ROW_BYTES = 608
 
 # Tensor ids for the seed sequences.
 _T_LENGTHS, _T_PAGES, _T_SCALE, _T_KV, _T_QNOPE, _T_QROPE, _T_PLANT = range(7)
@@ -53,9 +56,12 @@ def softmax_scale_default() -> float:
 
 def kv_bytes_per_token(kv_dtype: str) -> int:
     """Algorithmic KV bytes read per visible token: 576 elements (+ fp32 scale
-    for FP8); FP4 rows are 336 bytes (288 of codes, 36 block scales, padding)."""
+    for FP8); FP4 rows are 336 bytes (288 of codes, 36 block scales,
+    padding), MXFP8 rows 608 (576 codes, 18 block scales, padding)."""
     if kv_dtype == "fp4":
         return FP4_ROW_BYTES
+    if kv_dtype == "mxfp8":
+        return MXFP8_ROW_BYTES
     return D_K * 2 if kv_dtype == "bf16" else D_K * 1 + 4
 
 
@@ -89,13 +95,13 @@ class DecodeInputs:
     batch: int
     q_len: int
     num_heads: int
-    kv_dtype: str  # "bf16" | "fp8" | "fp4"
+    kv_dtype: str  # "bf16" | "fp8" | "fp4" | "mxfp8"
     page_size: int
     seq_lens: np.ndarray  # int64 [B], global lengths including the q drafts
     local_lens: np.ndarray  # int64 [B], table columns used on this shard
     q_nope: torch.Tensor  # bf16 [B, q, H, 512]
     q_rope: torch.Tensor  # bf16 [B, q, H, 64]
-    pool: torch.Tensor  # bf16 [S, 576], uint8 [S, 576] (e4m3fn) or uint8 [S, 336] (FP4)
+    pool: torch.Tensor  # bf16 [S, 576], uint8 [S, 576] (e4m3fn), [S, 336] (FP4) or [S, 608] (MXFP8)
     kv_scale: torch.Tensor | None  # float32 [S] (FP8 only)
     req_to_token: torch.Tensor  # int32 [B, stride]
     softmax_scale: float
@@ -196,6 +202,20 @@ def _fill_fp4(rows: int, gen, device, exp_lo: int, exp_hi: int) -> torch.Tensor:
     return out
 
 
+def _fill_mxfp8(rows: int, gen, device, exp_lo: int, exp_hi: int) -> torch.Tensor:
+    """MXFP8 rows: N(0, 1) rounded to e4m3fn codes, block-scale exponents
+    uniform in [exp_lo, exp_hi] (as codes 127 + e), zero padding."""
+    out = torch.zeros((rows, MXFP8_ROW_BYTES), dtype=torch.uint8, device=device)
+    out[:, :D_K] = _fill_values((rows, D_K), gen, device, "fp8", 1.0)
+    chunk = 1 << 18
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        out[r0:r1, D_K:D_K + 18] = torch.randint(
+            127 + exp_lo, 127 + exp_hi + 1, (r1 - r0, 18), generator=gen, device=device,
+            dtype=torch.int32).to(torch.uint8)
+    return out
+
+
 def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str,
                 page_size: int = 64, device="cpu", dcp_size: int = 1, dcp_rank: int = 0,
                 q_std: float = 0.1, kv_std: float = 0.1, scale_lo: float = 0.01,
@@ -220,6 +240,9 @@ def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str
         # Elements up to 6 * 2^-4; typical magnitudes near those of the BF16
         # pools (N(0, 1) * 0.1).
         pool = _fill_fp4(num_slots, kv_gen, device, -6, -4)
+    elif kv_dtype == "mxfp8":
+        # N(0, 1) * 2^(-5 .. -3): magnitudes near those of the BF16 pools.
+        pool = _fill_mxfp8(num_slots, kv_gen, device, -5, -3)
     else:
         pool = _fill_values((num_slots, D_K), kv_gen, device, kv_dtype, kv_std)
     kv_scale = None
@@ -244,10 +267,14 @@ def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str
             # its block scales up by 2^3 with it.
             pool[:, D_C // 2] = (pool[:, D_C // 2] & 0xF0) | 0x7
             pool[:, FP4_CODE_BYTES + D_C // 16] = 127 + 3
+        elif kv_dtype == "mxfp8":
+            # Element 512 = 448 * 2^-5 = 14 (its block at scale 2^-5).
+            pool[:, D_C] = 0x7E
+            pool[:, D_K + D_C // 32] = 127 - 5
         else:
             pool[:, D_C] = 0x7E  # e4m3fn 448
     elif variant == "planted":
-        if kv_dtype == "fp4":
+        if kv_dtype in ("fp4", "mxfp8"):
             raise ValueError("the planted variant is defined for BF16 and FP8 pools")
         rng = _np_rng(cfg_id, _T_PLANT, extra)
         q0 = torch.cat([qn[:, 0, 0].float(), qr[:, 0, 0].float()], dim=-1).cpu()  # [B, 576]
@@ -282,6 +309,9 @@ def _poison(pool, kv_scale, unused, kv_dtype: str) -> None:
     elif kv_dtype == "fp4":
         pool[unused, :FP4_CODE_BYTES] = FP4_POISON_CODES
         pool[unused, FP4_CODE_BYTES:FP4_CODE_BYTES + 36] = FP4_POISON_SCALE
+    elif kv_dtype == "mxfp8":
+        pool[unused, :D_K] = E4M3FN_NAN_CODE
+        pool[unused, D_K:D_K + 18] = FP4_POISON_SCALE
     else:
         pool[unused] = E4M3FN_NAN_CODE
         if kv_scale is not None:
