@@ -43,9 +43,9 @@ def mfma_peak_tflops(kv_dtype: str) -> float:
     RoPE part (2 * 64) on bf16 MFMAs, so the floor is the sum of the two
     times and the effective peak 2176 / (2048 / 5000 + 128 / 2500).  FP4 KV:
     the rows are dequantized exactly to BF16 and both products run on bf16
-    MFMAs.
+    MFMAs; the same for MXFP8 KV.
     """
-    if kv_dtype in ("bf16", "fp4"):
+    if kv_dtype in ("bf16", "fp4", "mxfp8"):
         return MFMA_BF16_PEAK_TFLOPS
     return 2176.0 / (2048.0 / MFMA_FP8_PEAK_TFLOPS + 128.0 / MFMA_BF16_PEAK_TFLOPS)
 B200_CONTEXT_US = {"mtp": 1240.0, "dcp8": 826.0}  # the pages' numbers (other hardware)
@@ -57,6 +57,7 @@ WORKLOADS = {
     "dcp8": 4,      # one shard of 128 x 100k over 8 shards, q5, h96, fp8
     "mtp-fp4": 6,   # the mtp shape over an FP4 pool
     "standard-fp4": 7,  # the standard shape over an FP4 pool
+    "mtp-mxfp8": 8,  # the mtp shape over an MXFP8 pool
 }
 
 
@@ -600,7 +601,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3+bf16", "fp4": "fp4_e2m1+bf16"}[x.kv_dtype],
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3+bf16", "fp4": "fp4_e2m1+bf16",
+                  "mxfp8": "mxfp8_e4m3+bf16"}[x.kv_dtype],
         "data": "synthetic",
         "config": {"workload": CONFIGS[cfg]["name"], "requests": x.batch,
                    "context": int(max(x.seq_lens)), "q_len": x.q_len, "heads": x.num_heads,

@@ -58,11 +58,21 @@ typedef enum {
  *   bytes 324..335  padding (ignored; rows stay 16-byte aligned).
  * Element value = e2m1(code) * 2^(c - 127).  A referenced row with a scale
  * code outside 63..191 gives an undefined result (no fault).
+ *
+ * MXFP8 (same page, "cell_size": one byte per element plus one scale per 32
+ * elements) is read as OCP e4m3fn codes with one power-of-two scale byte per
+ * 32 elements, 608 bytes a row:
+ *   bytes   0..575  the 576 codes, element i in byte i;
+ *   bytes 576..593  block scales, byte 576 + k for elements 32 k .. 32 k + 31,
+ *                   code c meaning 2^(c - 127), valid for 63 <= c <= 191;
+ *   bytes 594..607  padding (ignored).
+ * Element value = e4m3fn(code) * 2^(c - 127).
  */
 typedef enum {
-  MLA_KV_BF16 = 0,     /* pool element = bfloat16 */
-  MLA_KV_FP8_E4M3 = 1, /* pool element = OCP e4m3fn byte; fp32 scale per slot */
-  MLA_KV_FP4_E2M1 = 2  /* 336-byte rows of e2m1 codes and block scales (above) */
+  MLA_KV_BF16 = 0,       /* pool element = bfloat16 */
+  MLA_KV_FP8_E4M3 = 1,   /* pool element = OCP e4m3fn byte; fp32 scale per slot */
+  MLA_KV_FP4_E2M1 = 2,   /* 336-byte rows of e2m1 codes and block scales (above) */
+  MLA_KV_MXFP8_E4M3 = 3  /* 608-byte rows of e4m3fn codes and block scales (above) */
 } mla_kv_dtype;
 
 /* Problem description shared by the planner and the decode call. */
@@ -123,10 +133,11 @@ mla_status mla_decode_plan(const mla_decode_desc* desc, const int32_t* seq_lens_
  *   q_rope:          bf16 [B, q_len, H, 64], contiguous, device.
  *   kv_pool:         [num_slots, 576] contiguous, device; bf16 or e4m3fn bytes
  *                    per desc.kv_dtype; row = [c_kv (512) | k_rope (64)];
- *                    FP4: [num_slots, 336] bytes in the row format above.
+ *                    FP4: [num_slots, 336], MXFP8: [num_slots, 608] bytes in
+ *                    the row formats above.
  *                    1 <= num_slots <= 2^31 - 1.
  *   kv_scale:        fp32 [num_slots] for FP8 (value = e4m3fn(code) * scale),
- *                    ignored (may be NULL) for BF16 and FP4.
+ *                    ignored (may be NULL) for the other formats.
  *   req_to_token:    int32 [B, req_to_token_stride], device; column j holds the
  *                    pool slot of local index j (= position p when W == 1).
  *                    Slots outside [0, num_slots) are clamped (no fault, but the

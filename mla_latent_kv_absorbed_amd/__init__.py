@@ -7,7 +7,9 @@ marshals arguments.  See `decode`, `make_plan`, `lse_combine`, `prepare`.
 
 from ._binding import (  # noqa: F401
     KV_BF16,
+    KV_FP4,
     KV_FP8,
+    KV_MXFP8,
     DecodeDesc,
     MlaError,
     Plan,

@@ -17,8 +17,11 @@ import numpy as np
 KV_BF16 = 0
 KV_FP8 = 1
 KV_FP4 = 2
-_KV_CODES = {"bf16": KV_BF16, "fp8": KV_FP8, "fp4": KV_FP4}
+KV_MXFP8 = 3
+_KV_CODES = {"bf16": KV_BF16, "fp8": KV_FP8, "fp4": KV_FP4, "mxfp8": KV_MXFP8}
 FP4_ROW_BYTES = 336
+MXFP8_ROW_BYTES = 608
+_BLOCK_ROW_BYTES = {KV_FP4: FP4_ROW_BYTES, KV_MXFP8: MXFP8_ROW_BYTES}
 
 MLA_OK = 0
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape",
@@ -206,10 +209,10 @@ def decode(plan: Plan, q_nope, q_rope, kv_pool, kv_scale, req_to_token, seq_lens
             tuple(q_rope.shape) != (B, h["q_len"], h["num_heads"], 64):
         raise MlaError("query shapes do not match the plan")
     fp8 = h["kv_dtype"] == KV_FP8
-    if h["kv_dtype"] == KV_FP4:
-        if kv_pool.dtype != torch.uint8 or kv_pool.dim() != 2 or \
-                kv_pool.shape[1] != FP4_ROW_BYTES:
-            raise MlaError(f"FP4 pools must be uint8 [num_slots, {FP4_ROW_BYTES}]")
+    if h["kv_dtype"] in _BLOCK_ROW_BYTES:
+        rb = _BLOCK_ROW_BYTES[h["kv_dtype"]]
+        if kv_pool.dtype != torch.uint8 or kv_pool.dim() != 2 or kv_pool.shape[1] != rb:
+            raise MlaError(f"this plan's pools must be uint8 [num_slots, {rb}]")
     else:
         want_pool = torch.uint8 if fp8 else torch.bfloat16
         if kv_pool.dtype not in ((want_pool, torch.float8_e4m3fn) if fp8 else (want_pool,)) or \

@@ -7,14 +7,14 @@
 namespace mla {
 
 // Element type of the KV pool (the values of mla_kv_dtype).
-enum KvKind : int { kKvBf16 = 0, kKvFp8 = 1, kKvFp4 = 2 };
+enum KvKind : int { kKvBf16 = 0, kKvFp8 = 1, kKvFp4 = 2, kKvMx = 3 };
 
 // Arguments of the decode kernel (device pointers unless noted).
 struct DecodeArgs {
   const uint8_t* plan;       // device copy of the plan blob
   const uint16_t* q_nope;    // bf16 bits [B, M, 512]
   const uint16_t* q_rope;    // bf16 bits [B, M, 64]
-  const uint8_t* pool;       // [num_slots, 576] bf16 or e4m3fn elements; FP4: 336-byte rows
+  const uint8_t* pool;       // [num_slots, 576] bf16 or e4m3fn elements; FP4 / MXFP8 rows
   const float* kv_scale;     // [num_slots] (FP8)
   int64_t num_slots;
   const int32_t* table;      // [B, stride]

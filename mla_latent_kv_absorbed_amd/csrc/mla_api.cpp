@@ -35,7 +35,8 @@ namespace {
 using namespace mla;
 
 // launch_decode takes the plan's mla_kv_dtype as a KvKind.
-static_assert(kKvBf16 == MLA_KV_BF16 && kKvFp8 == MLA_KV_FP8_E4M3 && kKvFp4 == MLA_KV_FP4_E2M1,
+static_assert(kKvBf16 == MLA_KV_BF16 && kKvFp8 == MLA_KV_FP8_E4M3 && kKvFp4 == MLA_KV_FP4_E2M1 &&
+                  kKvMx == MLA_KV_MXFP8_E4M3,
               "KvKind and mla_kv_dtype differ");
 
 // Fixed cost of one work unit, in token-equivalents (Q load + O write).
@@ -55,7 +56,7 @@ mla_status check_desc(const mla_decode_desc* d) {
   if ((int64_t)d->q_len * d->num_heads > (1 << 20)) return MLA_ERR_INVALID_ARG;
   if (d->page_size < 1) return MLA_ERR_INVALID_ARG;
   if (d->kv_dtype != MLA_KV_BF16 && d->kv_dtype != MLA_KV_FP8_E4M3 &&
-      d->kv_dtype != MLA_KV_FP4_E2M1)
+      d->kv_dtype != MLA_KV_FP4_E2M1 && d->kv_dtype != MLA_KV_MXFP8_E4M3)
     return MLA_ERR_INVALID_ARG;
   if (d->dcp_size < 1 || d->dcp_rank < 0 || d->dcp_rank >= d->dcp_size)
     return MLA_ERR_INVALID_ARG;

@@ -51,7 +51,7 @@ def _desc(**kw):
 
 @pytest.mark.parametrize("bad", [dict(batch=0), dict(q_len=0), dict(q_len=9), dict(num_heads=0),
                                  dict(page_size=0), dict(dcp_size=0), dict(dcp_rank=8, dcp_size=8),
-                                 dict(dcp_rank=-1), dict(kv_dtype=7), dict(kv_dtype=3),
+                                 dict(dcp_rank=-1), dict(kv_dtype=7), dict(kv_dtype=4),
                                  dict(kv_dtype=-1), dict(num_cus=-1),
                                  dict(force_splits=-2)])
 def test_plan_rejects_invalid_descriptions(bad):
@@ -63,8 +63,9 @@ def test_plan_rejects_invalid_descriptions(bad):
 
 def test_plan_accepts_every_pool_format():
     # BF16, FP8 and FP4 pools plan alike (the work is in tokens, not bytes).
-    plans = [mla.make_plan(_desc(kv_dtype=kv), [3000, 40]) for kv in ("bf16", "fp8", "fp4")]
-    for p, code in zip(plans, (0, 1, 2)):
+    plans = [mla.make_plan(_desc(kv_dtype=kv), [3000, 40])
+             for kv in ("bf16", "fp8", "fp4", "mxfp8")]
+    for p, code in zip(plans, (0, 1, 2, 3)):
         assert p.header["kv_dtype"] == code
     assert len({p.header["num_units"] for p in plans}) == 1
     assert np.array_equal(plans[0].units(), plans[2].units())
@@ -73,7 +74,9 @@ def test_plan_accepts_every_pool_format():
 def test_fp4_format_constants_match_the_header():
     text = open(os.path.join(ROOT, "include", "mla.h")).read()
     assert re.search(r"MLA_KV_FP4_E2M1\s*=\s*2", text)
+    assert re.search(r"MLA_KV_MXFP8_E4M3\s*=\s*3", text)
     assert "336" in text and mla._binding.FP4_ROW_BYTES == 336
+    assert "608" in text and mla._binding.MXFP8_ROW_BYTES == 608
 
 
 def test_plan_rejects_unsupported_dims():
@@ -179,7 +182,7 @@ def test_prepare_rejects_bad_arguments_on_host():
     assert call(T=0, kv=0, scale=None) == 0
     assert call(T=-1) == -1
     assert call(H=0) == -1
-    assert call(kv=3) == -1                          # not a pool format (2 is FP4)
+    assert call(kv=4) == -1                          # not a pool format (3 is MXFP8)
     assert call(kv=-1) == -1
     assert call(max_pos=0) == -1
     assert call(nslots=0) == -1

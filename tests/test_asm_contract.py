@@ -224,9 +224,9 @@ def _blocks_with_depth(body):
     return blocks
 
 
-# decode_kernel<kKv, kPaged>: kKv 0 BF16, 1 FP8, 2 FP4.
+# decode_kernel<kKv, kPaged>: kKv 0 BF16, 1 FP8, 2 FP4, 3 MXFP8.
 @pytest.mark.parametrize("variant", ["ILi1ELb1E", "ILi1ELb0E", "ILi0ELb1E", "ILi0ELb0E",
-                                     "ILi2ELb1E", "ILi2ELb0E"])
+                                     "ILi2ELb1E", "ILi2ELb0E", "ILi3ELb1E", "ILi3ELb0E"])
 def test_tile_loops_do_not_spill(compiled, variant):
     # A scratch reload inside a tile loop is a VMEM load: waiting for it also
     # waits for every global->LDS DMA issued before it, which serialises the

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_O_MAX, TOL_O_REL, TOL_LSE = 2e-2, 1e-2, 1e-3
 DEV = "cuda"
-KV_DTYPES = ["bf16", "fp8", "fp4"]
+KV_DTYPES = ["bf16", "fp8", "fp4", "mxfp8"]
 
 
 def oracle(x, reqs=None, **kw):
@@ -100,7 +100,7 @@ def test_rows_past_the_request_end(kv, q, H, splits):
 @pytest.mark.parametrize("q", [1, 5])
 @pytest.mark.parametrize("splits", [1, 2, 7, 40])
 def test_peaked_variants_and_forced_splits(kv, variant, q, splits):
-    if kv == "fp4" and variant == "planted":
+    if kv in ("fp4", "mxfp8") and variant == "planted":
         pytest.skip("the planted variant is defined for BF16 and FP8 pools only")
     x = make_inputs(50, [1300, 257], q, 32, kv, variant=variant,
                     kv_std=0.1 if kv == "bf16" else 1.0)
@@ -304,3 +304,33 @@ def test_fp4_standard_workload_full():
     x = config_inputs(7, device=DEV)
     out, lse = gpu_decode(x)
     check(out, lse, *oracle(x), tag="standard 32x4096 q1 h128 fp4 (all requests)")
+
+
+def test_mxfp8_every_code_and_scale_decodes_exactly():
+    # One visible token, q_len 1, zero query: O is that token's c_kv, whose
+    # 32-element blocks hold every finite e4m3fn code under block scales
+    # spanning the valid range 2^-64 .. 2^64.
+    from oracle import decode_mxfp8_rows
+    x = make_inputs(68, [1], 1, 32, "mxfp8")
+    x.q_nope.zero_()
+    x.q_rope.zero_()
+    slot = int(x.req_to_token[0, 0])
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    row = np.zeros(608, dtype=np.uint8)
+    row[:512] = np.resize(np.concatenate([finite, finite[::-1]]), 512)
+    row[512:576] = finite[:64]
+    row[576:592] = np.linspace(63, 191, 16).round().astype(np.uint8)
+    row[592:594] = 127
+    x.pool[slot] = torch.from_numpy(row)
+    out, lse = gpu_decode(x, force_splits=1)
+    o = out[0, 0].double().cpu().numpy()
+    want = decode_mxfp8_rows(row[None])[0, :512]
+    np.testing.assert_allclose(o, np.broadcast_to(want, o.shape), rtol=1e-5, atol=0)
+
+
+def test_mxfp8_mtp_100k_workload_sampled():
+    x = config_inputs(8, device=DEV)
+    out, lse = gpu_decode(x)
+    reqs = [0, 11]
+    o_ref, l_ref = oracle(x, reqs=reqs)
+    check(out[reqs], lse[reqs], o_ref, l_ref, tag="mtp 16x100k q5 h96 mxfp8 (requests 0, 11)")

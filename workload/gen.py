@@ -354,7 +354,8 @@ def shard_from_full(full: DecodeInputs, dcp_size: int, dcp_rank: int,
         dcp_size=W, dcp_rank=r, name=f"{full.name}/shard{r}", meta=dict(full.meta, shard=r))
 
 
-# The five workloads, and two FP4-pool companions of the same shapes (6, 7).
+# The five workloads, and companions of the same shapes over FP4 pools (6, 7)
+# and an MXFP8 pool (8).
 # Each is a decode call (or, for DCP, eight shard calls and one merge) on one
 # GPU.
 CONFIGS = {
@@ -372,6 +373,8 @@ CONFIGS = {
             kv_dtype="fp4"),
     7: dict(name="standard-32x4096-q1-h128-fp4", seq_lens=[4096] * 32, q_len=1,
             num_heads=128, kv_dtype="fp4"),
+    8: dict(name="mtp-16x100k-q5-h96-mxfp8", seq_lens=[100000] * 16, q_len=5, num_heads=96,
+            kv_dtype="mxfp8"),
 }
 SWEEP_BATCHES = (1, 2, 4, 8, 12, 16, 20, 24)
 
