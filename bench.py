@@ -127,9 +127,9 @@ def prepare_bytes(x) -> float:
     """Algorithmic HBM bytes of one mla_prepare call: w_kc read once, the
     queries read and written once, the new rows and their positions' cos /
     sin read once, and the pool rows (and FP8 scales) written once (FP4: 336
-    bytes a row)."""
+    bytes a row, MXFP8: 608)."""
     T, H = x["T"], x["H"]
-    row = {"bf16": 576 * 2, "fp8": 576 + 4, "fp4": 336}[x["kv_dtype"]]
+    row = {"bf16": 576 * 2, "fp8": 576 + 4, "fp4": 336, "mxfp8": 608}[x["kv_dtype"]]
     return float(H * 512 * 128 * 2 + T * H * 128 * 2 + 2 * T * H * 64 * 2 + T * H * 512 * 2
                  + T * 576 * 2 + T * 64 * 4 + T * row + T * 8)
 

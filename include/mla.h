@@ -217,7 +217,8 @@ mla_status mla_lse_combine(const float* part_o, const float* part_lse, int32_t n
  *       the exponent e is the smallest integer with a <= 6 * 2^e, clamped to
  *       [-64, 64] (a = 0 gives -64), and each code is the e2m1 value nearest
  *       to x * 2^-e (ties to the code with an even mantissa bit, clamped to
- *       +-6); the padding bytes are written as zeros.
+ *       +-6); the padding bytes are written as zeros; or for MXFP8 pools the
+ *       same per 32-element block with 448 in place of 6 and e4m3fn codes.
  *
  * RoPE rotates the interleaved pairs (x[2i], x[2i+1]) of a 64-wide vector:
  * (x0 c - x1 s, x0 s + x1 c) with c = cos_sin[pos, i], s = cos_sin[pos, 32 + i];
@@ -250,9 +251,10 @@ mla_status mla_lse_combine(const float* part_o, const float* part_lse, int32_t n
  *   q_nope_absorbed: bf16 [T, H, 512] device output.
  *   q_rope_out:      bf16 [T, H, 64] device output (must not alias q_rope_in).
  *   kv_pool:         [num_slots, 576] device pool (as for mla_decode; FP4:
- *                    [num_slots, 336] bytes), written at the stored slots only.
+ *                    [num_slots, 336], MXFP8: [num_slots, 608] bytes), written
+ *                    at the stored slots only.
  *   kv_scale:        fp32 [num_slots] device for FP8 pools (written at the
- *                    stored slots), NULL for BF16 and FP4.
+ *                    stored slots), NULL for the other formats.
  *   stream:          HIP stream, 0 = default stream.
  *
  * All pointers 16-byte aligned (kv_scale 4-byte).  Errors are detected on the

@@ -279,7 +279,7 @@ def prepare(q_nope, q_rope_in, w_kc_t, c_kv_new, k_rope_new, positions, cos_sin,
     c_kv_new [T, 512], k_rope_new [T, 64] (bf16); positions, slots int32 [T];
     cos_sin fp32 [max_pos, 64]; kv_pool [num_slots, 576] (bf16, or uint8 /
     float8_e4m3fn with an fp32 kv_scale [num_slots]), or uint8 [num_slots,
-    336] for FP4 rows.  Returns
+    336] for FP4 rows, [num_slots, 608] for MXFP8 rows.  Returns
     (q_nope_absorbed [T, H, 512], q_rope_out [T, H, 64]); the pool rows at
     `slots` (and their scales) are written in place.
     """
@@ -297,13 +297,15 @@ def prepare(q_nope, q_rope_in, w_kc_t, c_kv_new, k_rope_new, positions, cos_sin,
     if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != 64 or \
             not cos_sin.is_contiguous():
         raise MlaError("cos_sin must be a contiguous float32 [max_pos, 64] tensor")
-    fp4 = kv_pool.dtype == torch.uint8 and kv_pool.dim() == 2 and \
-        kv_pool.shape[1] == FP4_ROW_BYTES
-    fp8 = not fp4 and kv_pool.dtype in (torch.uint8, torch.float8_e4m3fn)
-    if kv_pool.dim() != 2 or not (fp4 or (kv_pool.shape[1] == 576 and
-                                          (fp8 or kv_pool.dtype == bf))):
+    block = None
+    if kv_pool.dtype == torch.uint8 and kv_pool.dim() == 2:
+        block = {FP4_ROW_BYTES: KV_FP4, MXFP8_ROW_BYTES: KV_MXFP8}.get(int(kv_pool.shape[1]))
+    fp8 = block is None and kv_pool.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if kv_pool.dim() != 2 or not (block is not None or (kv_pool.shape[1] == 576 and
+                                                        (fp8 or kv_pool.dtype == bf))):
         raise MlaError("kv_pool must be [num_slots, 576] of bf16 or e4m3fn bytes, or "
-                       f"uint8 [num_slots, {FP4_ROW_BYTES}] FP4 rows")
+                       f"uint8 [num_slots, {FP4_ROW_BYTES}] FP4 / [num_slots, "
+                       f"{MXFP8_ROW_BYTES}] MXFP8 rows")
     if fp8 and (kv_scale is None or kv_scale.dtype != torch.float32):
         raise MlaError("FP8 pools need an fp32 kv_scale per slot")
     if q_nope_absorbed is None:
@@ -311,7 +313,7 @@ def prepare(q_nope, q_rope_in, w_kc_t, c_kv_new, k_rope_new, positions, cos_sin,
     if q_rope_out is None:
         q_rope_out = torch.empty((T, H, 64), dtype=bf, device=dev)
     st = load_library().mla_prepare(
-        T, H, KV_FP4 if fp4 else (KV_FP8 if fp8 else KV_BF16), _ptr(q_nope), _ptr(q_rope_in), _ptr(w_kc_t),
+        T, H, block if block is not None else (KV_FP8 if fp8 else KV_BF16), _ptr(q_nope), _ptr(q_rope_in), _ptr(w_kc_t),
         _ptr(c_kv_new), _ptr(k_rope_new), _ptr(positions), _ptr(cos_sin), int(cos_sin.shape[0]),
         _ptr(slots), _ptr(q_nope_absorbed), _ptr(q_rope_out), _ptr(kv_pool),
         _ptr(kv_scale if fp8 else None), int(kv_pool.shape[0]), _stream(stream))

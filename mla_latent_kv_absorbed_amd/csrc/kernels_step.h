@@ -13,7 +13,7 @@ struct PrepareArgs {
   int T;                        // new tokens
   int H;                        // heads
   int max_pos;                  // rows of cos_sin
-  int kv;                       // pool format (mla_kv_dtype values: 0 BF16, 1 FP8, 2 FP4)
+  int kv;                       // pool format (mla_kv_dtype: 0 BF16, 1 FP8, 2 FP4, 3 MXFP8)
   int64_t num_slots;
   const uint16_t* q_nope;       // bf16 bits [T, H, 128]
   const uint16_t* q_rope_in;    // bf16 bits [T, H, 64]
@@ -25,7 +25,7 @@ struct PrepareArgs {
   const int32_t* slots;         // [T]
   uint16_t* q_nope_absorbed;    // bf16 bits [T, H, 512]
   uint16_t* q_rope_out;         // bf16 bits [T, H, 64]
-  void* pool;                   // [num_slots, 576] bf16 bits or e4m3fn codes; FP4 336-byte rows
+  void* pool;                   // [num_slots, 576] bf16 bits or e4m3fn codes; FP4 / MXFP8 rows
   float* kv_scale;              // [num_slots] (FP8)
 };
 

@@ -121,7 +121,8 @@ mla_status mla_prepare(int32_t num_tokens, int32_t num_heads, int32_t kv_dtype,
                        void* q_nope_absorbed, void* q_rope_out, void* kv_pool, float* kv_scale,
                        int64_t num_slots, void* stream) {
   if (num_tokens < 0 || num_heads < 1 || max_pos < 1 || num_slots < 1) return MLA_ERR_INVALID_ARG;
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_FP4_E2M1)
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_FP4_E2M1 &&
+      kv_dtype != MLA_KV_MXFP8_E4M3)
     return MLA_ERR_INVALID_ARG;
   const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
   for (const void* p : {q_nope, q_rope_in, w_kc_t, c_kv_new, k_rope_new, (const void*)positions,

@@ -13,7 +13,9 @@
 //                   at the given slots: BF16 bits, e4m3fn codes with the
 //                   per-token scale amax / 448, or FP4 rows (e2m1 codes with
 //                   a power-of-two scale per 16 elements; page "resident
-//                   VRAM accounting", sections "KV ledger" and "cell_size").
+//                   VRAM accounting", sections "KV ledger" and "cell_size"),
+//                   or MXFP8 rows (e4m3fn codes with a power-of-two scale
+//                   per 32 elements; same page, "cell_size").
 //
 // Every float32 step that decides a stored bit (the roped values, the scale,
 // the quotients) is a correctly rounded IEEE operation with no contraction,
@@ -195,6 +197,54 @@ __device__ __forceinline__ void append_fp4(uint8_t* row, int tid, float c0, floa
   }
 }
 
+// MXFP8 row of one token: thread i holds elements 2 i, 2 i + 1 of c_kv and
+// threads 0..31 also elements 512 + 2 i, + 1 of the roped k_rope.  Block k
+// (32 elements) lies in threads 16 k .. 16 k + 15 (c_kv blocks 0..15;
+// k_rope blocks 16, 17 in threads 0..15 and 16..31).  Its exponent e is the
+// smallest with amax <= 448 * 2^e: with amax = f 2^E (0.5 <= f < 1) and 448 =
+// 0.875 * 2^9, e = E - 9 if f <= 0.875, else E - 8; clamped to [-64, 64]
+// (amax below 2^-100 takes -64).  Codes: e4m3fn nearest to x 2^-e (exact),
+// ties to even, clamped to +-448.
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  if (!(amax >= 0x1p-100f)) return -64;
+  const float f = __builtin_amdgcn_frexp_mantf(amax);
+  const int E = __builtin_amdgcn_frexp_expf(amax);
+  const int e = f <= 0.875f ? E - 9 : E - 8;
+  return e > 64 ? 64 : (e < -64 ? -64 : e);
+}
+
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t mx_pair(float a, float b, int e) {
+  const float ya = fminf(fmaxf(__builtin_amdgcn_ldexpf(a, -e), -448.0f), 448.0f);
+  const float yb = fminf(fmaxf(__builtin_amdgcn_ldexpf(b, -e), -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ya, yb, 0, false) & 0xffffu;
+}
+
+__device__ __forceinline__ void append_mx(uint8_t* row, int tid, float c0, float c1, float r0,
+                                          float r1) {
+  const int ec = mx_block_exponent(max16(fmaxf(fabsf(c0), fabsf(c1))));
+  const int er = mx_block_exponent(max16(fmaxf(fabsf(r0), fabsf(r1))));  // wave 0 lanes 0..31
+  uint16_t* row16 = reinterpret_cast<uint16_t*>(row);
+  uint32_t* row32 = reinterpret_cast<uint32_t*>(row);
+  row16[tid] = (uint16_t)mx_pair(c0, c1, ec);                      // bytes 0..511
+  const uint32_t scales = gather4((uint32_t)(ec + 127), 16);
+  const uint32_t rscales = (uint32_t)(er + 127) | ((uint32_t)__shfl_down(er + 127, 16) << 8);
+  if ((tid & 63) == 0) row32[144 + (tid >> 6)] = scales;           // bytes 576..591
+  if (tid < 32) {
+    row16[256 + tid] = (uint16_t)mx_pair(r0, r1, er);               // bytes 512..575
+    if (tid == 0) row16[296] = (uint16_t)rscales;                   // bytes 592, 593
+  } else if (tid == 32) {
+    row16[297] = 0;                                                  // padding 594..595
+  } else if (tid < 36) {
+    row32[149 + (tid - 33)] = 0u;                                    // padding 596..607
+  }
+}
+
 // One block per new token.  Threads 0..255 rotate the token's q_rope pairs
 // (H x 32 of them), then thread i takes c_kv elements 2 i, 2 i + 1 and
 // threads 0..31 the k_rope pair i of the row to append.
@@ -221,10 +271,15 @@ __device__ __forceinline__ void rope_append_block(const PrepareArgs& a, int t, f
     const uint32_t kin = reinterpret_cast<const uint32_t*>(a.k_rope_new + (int64_t)t * 64)[tid];
     kr = rope_pair(kin, c, s);
   }
-  if (a.kv == 2) {
+  if (a.kv == 2 || a.kv == 3) {
     const float r0 = tid < 32 ? bf16_lo(kr) : 0.f, r1 = tid < 32 ? bf16_hi(kr) : 0.f;
-    append_fp4(static_cast<uint8_t*>(a.pool) + slot * 336, tid, bf16_lo(ckv), bf16_hi(ckv), r0,
-               r1);
+    if (a.kv == 2) {
+      append_fp4(static_cast<uint8_t*>(a.pool) + slot * 336, tid, bf16_lo(ckv), bf16_hi(ckv),
+                 r0, r1);
+    } else {
+      append_mx(static_cast<uint8_t*>(a.pool) + slot * 608, tid, bf16_lo(ckv), bf16_hi(ckv),
+                r0, r1);
+    }
     return;
   }
   if (a.kv == 0) {

@@ -25,12 +25,12 @@ def _bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4", "mxfp8"])
 def test_prepare_then_decode(kv):
     q, H = 5, 16
     x = make_inputs(71, [300, 97, 5], q, H, kv, kv_std=0.1 if kv == "bf16" else 1.0)
     B = x.batch
-    rng = np.random.default_rng(np.random.SeedSequence([72, ord(kv[-1])]))
+    rng = np.random.default_rng(np.random.SeedSequence([72, len(kv), ord(kv[-1])]))
 
     def bf16(shape, std):
         return torch.from_numpy((rng.standard_normal(shape) * std).astype(np.float32)).to(

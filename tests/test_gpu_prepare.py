@@ -46,8 +46,9 @@ def _case(seed, T, H, kv, num_slots=None, max_pos=4096, skip=True):
     if kv == "bf16":
         x["kv_pool"] = bf16((num_slots, 576), 1.0)
         x["kv_scale"] = None
-    elif kv == "fp4":
-        x["kv_pool"] = torch.from_numpy(rng.integers(0, 256, (num_slots, 336)).astype(np.uint8))
+    elif kv in ("fp4", "mxfp8"):
+        rb = 336 if kv == "fp4" else 608
+        x["kv_pool"] = torch.from_numpy(rng.integers(0, 256, (num_slots, rb)).astype(np.uint8))
         x["kv_scale"] = None
     else:
         x["kv_pool"] = torch.from_numpy(rng.integers(0, 0x7E, (num_slots, 576)).astype(np.uint8))
@@ -93,13 +94,13 @@ def _check(x, kv, tag):
                                       err_msg=f"{tag}: scales")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4", "mxfp8"])
 @pytest.mark.parametrize("T,H", [(80, 96), (37, 128), (1, 16), (640, 96), (33, 1)])
 def test_prepare_matches_oracle(kv, T, H):
     _check(_case(10 * T + H, T, H, kv), kv, f"{kv} T{T} H{H}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4", "mxfp8"])
 def test_prepare_edge_inputs(kv):
     x = _case(5, 12, 8, kv, max_pos=64)
     pos = x["positions"].numpy()
@@ -136,3 +137,24 @@ def test_prepare_fp4_block_edges():
         c[t, 80:] = np.random.default_rng(t).standard_normal(432) * 2.0 ** e
     x["c_kv_new"] = torch.from_numpy(c).to(torch.bfloat16)
     _check(x, "fp4", "fp4 block edges")
+
+
+def test_prepare_mxfp8_block_edges():
+    # MXFP8 blocks whose largest value sits exactly on 448 * 2^e and one BF16
+    # ulp above it, values halfway between e4m3 neighbours (ties to even) and
+    # one ulp off, subnormal-range values, a block of tiny values and a
+    # saturating block.
+    x = _case(7, 8, 4, "mxfp8")
+    c = np.zeros((8, 512), np.float32)
+    for t in range(8):
+        e = 2 * t - 8
+        c[t, 0] = 448.0 * 2.0 ** e
+        c[t, 32] = (448.0 + 2.0) * 2.0 ** e                 # 448 + 1 BF16 ulp
+        c[t, 1:5] = np.array([1.0 + 1 / 16, 1.0 + 3 / 16, 3.0 + 1 / 8, 2.0 ** -7], np.float32) * 2.0 ** e
+        c[t, 5:9] = np.array([1.0 + 1 / 16 + 2 ** -7, 1.25 + 1 / 16, 2.0 ** -9 * 1.5, -2.0 ** -10],
+                             np.float32) * 2.0 ** e
+        c[t, 64:96] = 1e-30
+        c[t, 96:128] = 3e38 if t == 0 else 1.0
+        c[t, 128:] = np.random.default_rng(t).standard_normal(384) * 2.0 ** e
+    x["c_kv_new"] = torch.from_numpy(c).to(torch.bfloat16)
+    _check(x, "mxfp8", "mxfp8 block edges")

@@ -406,6 +406,7 @@ PREPARE_CONFIGS = {
     "dcp8": dict(name="prepare-dcp8-640x96-fp8", T=128 * 5, H=96, kv_dtype="fp8"),
     "standard": dict(name="prepare-standard-32x128-bf16", T=32, H=128, kv_dtype="bf16"),
     "mtp-fp4": dict(name="prepare-mtp-80x96-fp4", T=16 * 5, H=96, kv_dtype="fp4"),
+    "mtp-mxfp8": dict(name="prepare-mtp-80x96-mxfp8", T=16 * 5, H=96, kv_dtype="mxfp8"),
 }
 
 
@@ -428,8 +429,9 @@ def prepare_inputs(key: str, device="cpu", num_slots: int = 1 << 18, max_pos: in
     if kv == "bf16":
         x["kv_pool"] = torch.zeros((num_slots, 576), dtype=torch.bfloat16)
         x["kv_scale"] = None
-    elif kv == "fp4":
-        x["kv_pool"] = torch.zeros((num_slots, FP4_ROW_BYTES), dtype=torch.uint8)
+    elif kv in ("fp4", "mxfp8"):
+        rb = FP4_ROW_BYTES if kv == "fp4" else MXFP8_ROW_BYTES
+        x["kv_pool"] = torch.zeros((num_slots, rb), dtype=torch.uint8)
         x["kv_scale"] = None
     else:
         x["kv_pool"] = torch.zeros((num_slots, 576), dtype=torch.uint8)
