@@ -1,12 +1,14 @@
 """Generates tile_asm.inc: the tile work of the decode loop as inline-asm
-statements in which LDS reads, FP8 widening, the softmax, global->LDS DMA and
-MFMAs are software-pipelined by hand.
+statements in which LDS reads, the softmax, the FP4 dequantization,
+global->LDS DMA and MFMAs are software-pipelined by hand.
 
 Building blocks of a statement (any combination):
 
-  QK    S^T = K . Q^T of one tile: 36 MFMAs 32x32x16 bf16 (FP8 K widened
-        from e4m3fn codes in registers)
-  PV    O^T += V^T . P^T of one tile: 32 MFMAs (FP8 V^T widened in registers)
+  QK    S^T = K . Q^T of one tile: BF16 36 MFMAs 32x32x16; FP8 16 scaled
+        MFMAs 32x32x64 on the stored codes against two e4m3 terms of Q, plus
+        the RoPE part on 4 BF16 MFMAs (its codes widened in registers)
+  PV    O^T += V^T . P^T of one tile: BF16 32 MFMAs; FP8 16 scaled MFMAs
+        (the codes against two e4m3 terms of P)
   SM    the online softmax of one tile, given its scores: scale, max, the
         lazy rescale decision, exponentials, row sum and P packed to BF16
   DMA   the global->LDS copy of a later tile (row instructions)
@@ -26,7 +28,8 @@ Statements (T = BF16 or FP8):
 
 QK and PV MFMAs alternate one for one, so the dependent S chain never stalls
 the matrix pipe while PV MFMAs remain, and the VALU and LDS work (widening,
-softmax) issues between MFMAs, in the shadow of the one that is running.  A
+softmax, dequantization) issues between MFMAs, in the shadow of the one that
+is running.  A
 small list scheduler (below) assigns scratch registers in rings, issues each
 LDS read as early as its ring slot allows, waits for it with the exact lgkmcnt
 (LDS operations complete in issue order), keeps every VALU result two
@@ -122,13 +125,12 @@ class Read:
 
 
 class Op:
-    def __init__(self, kind, mfma, read, cvt_dw=None, acc=None, xoff=0):
+    def __init__(self, kind, mfma, read, acc=None, xoff=0):
         self.kind = kind        # "K" or "V"
         self.xoff = xoff        # first register of the A operand within the read's slot
         self.acc = acc
         self.mfma = mfma        # template: {acc} {x} {x3} {c}
         self.read = read        # rid feeding the A operand
-        self.cvt_dw = cvt_dw    # widened FP8: first dword of the codes in the read
 
 
 class Stream:
@@ -519,10 +521,6 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
     slot_of = {rid: k for q in queue.values() for k, rid in enumerate(q)}
     nxt = {ring: 0 for ring in queue}
     issued, freed = set(), set()
-    cvt_slot = {}
-    widened = {}
-    ring_next = {"C": 0}
-    slot_last_user = {}
     state = {"pos": -1}  # last issued MFMA
 
     def slot_free(ring):
@@ -580,35 +578,9 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
             widened_inplace.add(rid)
 
     def release_direct(rid):
-        rd = reads[rid]
-        if all(ops[u].cvt_dw is None for u in rd.users):  # in-place widening included
-            if all(u <= state["pos"] - 1 for u in rd.users):
-                freed.add(rid)
-
-    def widen(i):
-        op = ops[i]
-        key = (op.read, op.cvt_dw)
-        if key in widened:
-            cvt_slot[i] = widened[key]
-            return
-        rd = reads[op.read]
-        ensure(op.read)
-        slot = ring_next["C"] % rings["C"][0]
-        ring_next["C"] += 1
-        prev = slot_last_user.get(slot)
-        assert prev is None or prev <= state["pos"] - 1, f"C slot {slot} still read by MFMA {prev}"
-        src = st.reg(rd.ring, slot_of[op.read]) + op.cvt_dw
-        dst = st.reg("C", slot)
-        st.emit(f"v_cvt_scalef32_pk_bf16_fp8 v{dst}, v{src}, 1.0")
-        st.emit(f"v_cvt_scalef32_pk_bf16_fp8 v{dst + 1}, v{src}, 1.0 op_sel:[1,0,0]")
-        st.emit(f"v_cvt_scalef32_pk_bf16_fp8 v{dst + 2}, v{src + 1}, 1.0")
-        st.emit(f"v_cvt_scalef32_pk_bf16_fp8 v{dst + 3}, v{src + 1}, 1.0 op_sel:[1,0,0]")
-        st.last_valu[dst] = len(st.lines)
-        widened[key] = slot
-        cvt_slot[i] = slot
-        slot_last_user[slot] = max(j for j in range(n) if (ops[j].read, ops[j].cvt_dw) == key)
-        if all((ops[u].read, ops[u].cvt_dw) in widened for u in rd.users):
-            freed.add(op.read)
+        # A read's ring slot is free once every MFMA that reads it has issued.
+        if all(u <= state["pos"] - 1 for u in reads[rid].users):
+            freed.add(rid)
 
     sm_lds_slot = {}
 
@@ -653,18 +625,10 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
 
     started = set()
     fill()
-    if ops and ops[0].cvt_dw is not None:
-        widen(0)
     for i, op in enumerate(ops):
-        if op.cvt_dw is not None:
-            if i not in cvt_slot:
-                widen(i)
-            x = st.reg("C", cvt_slot[i])
-            gap = len(st.lines) - st.last_valu[x]
-        else:
-            ensure(op.read)
-            x = st.reg(reads[op.read].ring, slot_of[op.read]) + op.xoff
-            gap = len(st.lines) - st.last_valu[x] if x in st.last_valu else 2
+        ensure(op.read)
+        x = st.reg(reads[op.read].ring, slot_of[op.read]) + op.xoff
+        gap = len(st.lines) - st.last_valu[x] if x in st.last_valu else 2
         if gap < 2:
             st.emit(f"s_nop {1 - gap}")
         if op.kind == "K":
@@ -682,8 +646,6 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
             st.emit(f"@GLD({128 * k})")
         if i >= 1:
             sm_emit(per_slot, i)
-        if i + 1 < n and ops[i + 1].cvt_dw is not None:
-            widen(i + 1)
         fill()
     sm_emit(len(smp))
     for rid in reads:
