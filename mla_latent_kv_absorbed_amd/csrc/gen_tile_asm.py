@@ -19,6 +19,7 @@ Statements (T = BF16 or FP8):
   MLA_FUSED_BF16_ASM QK of tile t+1 and PV of tile t, plus DMA
   MLA_FUSED_BF16_NODMA_ASM  the same without the DMA (FP4 pools)
   MLA_FUSED_BF16_DQ_ASM  the same plus the dequantization of a raw FP4 tile
+  MLA_DQ_FP4_ASM     that dequantization alone (a wave with no rows)
   MLA_PV_T_ASM       PV (last tile of a unit)
   FP8, pipelined one tile deeper so that the softmax runs in the MFMA shadow:
   MLA_QKSM_FP8_ASM   QK of tile t+1 and SM of tile t, plus DMA (first step)
@@ -708,6 +709,8 @@ STATEMENTS = (
     # after next inside the statement.
     ("MLA_FUSED_BF16_NODMA_ASM", dict(fp8=False, qk=True, pv=True)),
     ("MLA_FUSED_BF16_DQ_ASM", dict(fp8=False, qk=True, pv=True, dq=True)),
+    # The dequantization alone: the share of a wave with no rows to compute.
+    ("MLA_DQ_FP4_ASM", dict(fp8=False, qk=False, pv=False, dq=True)),
 )
 
 
