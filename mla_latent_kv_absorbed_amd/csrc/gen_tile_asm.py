@@ -20,6 +20,7 @@ Statements (T = BF16 or FP8):
   MLA_FUSED_BF16_NODMA_ASM  the same without the DMA (FP4 pools)
   MLA_FUSED_BF16_DQ_ASM  the same plus the dequantization of a raw FP4 tile
   MLA_DQ_FP4_ASM     that dequantization alone (a wave with no rows)
+  MLA_FUSED_BF16_DQMX_ASM, MLA_DQ_MX_ASM  the same two for a raw MXFP8 tile
   MLA_PV_T_ASM       PV (last tile of a unit)
   FP8, pipelined one tile deeper so that the softmax runs in the MFMA shadow:
   MLA_QKSM_FP8_ASM   QK of tile t+1 and SM of tile t, plus DMA (first step)
@@ -406,8 +407,90 @@ def dq_program(base: int):
     return prog
 
 
+def dq_program_mx(base: int):
+    """Dequantization of one raw MXFP8 tile into the BF16 tile layout (the
+    MXFP8 counterpart of dq_program).
+
+    Raw tile: code chunk c (16 e4m3fn codes, elements 16 c .. + 16, block
+    c / 2) of token t at 512 c + 16 t; the scale byte of block b at 512 (36 +
+    b / 16) + 16 t + b % 16.  Code chunk c becomes BF16 chunks 2 c and 2 c +
+    1.  Lane (t, h) of wave w converts code chunks 2 w + h + 8 k (k = 0..3)
+    whole, in halves of 8 bytes (one BF16 chunk each), and half h of code
+    chunk 32 + w: every lane 4.5 chunks.  Scalars: %[dqa] = raw + 1024 w,
+    %[dqb] = raw + w, %[dqc] = bf16 tile + 2048 w, %[dqd] = raw + 512 w,
+    %[dqe] = raw + w / 2, %[dqf] = bf16 tile + 1024 w, %[dqg] = 128 (w % 2).
+    Scratch as in dq_program.
+    """
+    if base % 2:
+        SC, C, O, T, T2, TT, HH = base, base + 1, base + 3, base + 5, base + 6, base + 7, base + 8
+    else:
+        C, O, SC, T, T2, TT, HH = base, base + 2, base + 4, base + 5, base + 6, base + 7, base + 8
+    prog = []
+
+    def valu(text):
+        prog.append(("valu", text, [], [], None))
+
+    def lds(text, tag):
+        prog.append(("lds", text, [], [], tag))
+
+    def wait(tag):
+        prog.append(("wait", "", [], [], tag))
+
+    def convert_half(write_addr, off):
+        # 8 codes (two dwords) -> one 16-byte BF16 chunk, written in halves
+        for d in (0, 1):
+            for hi in (0, 1):
+                sel = " op_sel:[1,0,0]" if hi else ""
+                valu(f"v_cvt_scalef32_pk_bf16_fp8 v{O + hi}, v{C + d}, v{SC}{sel}")
+            lds(f"ds_write_b64 {write_addr}, v[{O}:{O + 1}] offset:{off + 8 * d}", ("DQW",))
+
+    valu(f"v_mbcnt_lo_u32_b32 v{TT}, -1, 0")
+    valu(f"v_mbcnt_hi_u32_b32 v{TT}, -1, v{TT}")
+    valu(f"v_and_b32 v{HH}, 32, v{TT}")                 # 32 h
+    valu(f"v_and_b32 v{TT}, 31, v{TT}")
+    valu(f"v_lshlrev_b32 v{TT}, 4, v{TT}")              # 16 t
+    for k in range(4):
+        # code chunk c = 2 w + h + 8 k, block w + 4 k
+        tag = ("DQM", k)
+        valu(f"v_add_u32 v{T}, %[dqb], v{TT}")
+        lds(f"ds_read_u8 v{SC}, v{T} offset:{512 * 36 + 4 * k}", tag + ("s",))
+        for q in (0, 1):
+            valu(f"v_lshl_add_u32 v{T}, v{HH}, 4, v{TT}")               # 16 t + 512 h
+            valu(f"v_add_u32 v{T}, %[dqa], v{T}")
+            lds(f"ds_read_b64 v[{C}:{C + 1}], v{T} offset:{4096 * k + 8 * q}", tag + ("c", q))
+            if q == 0:
+                wait(tag + ("s",))
+                valu(f"v_lshlrev_b32 v{SC}, 23, v{SC}")
+            wait(tag + ("c", q))
+            # BF16 chunk 4 w + 2 h + 16 k + q; its index & 3 is 2 h + q
+            valu(f"v_lshlrev_b32 v{T2}, 2, v{HH}")                     # 128 h
+            valu(f"v_xor_b32 v{T2}, v{T2}, v{TT}")
+            if q:
+                valu(f"v_xor_b32 v{T2}, 64, v{T2}")
+            valu(f"v_lshl_add_u32 v{T2}, v{HH}, 5, v{T2}")            # + 1024 * 2 h
+            valu(f"v_add_u32 v{T2}, %[dqc], v{T2}")
+            convert_half(f"v{T2}", 8192 * k + 512 * q)
+    # half h of code chunk 32 + w (block 16 + w / 2): BF16 chunk 64 + 2 w + h
+    tag = ("DQM", 4)
+    valu(f"v_add_u32 v{T}, %[dqe], v{TT}")
+    lds(f"ds_read_u8 v{SC}, v{T} offset:{512 * 37}", tag + ("s",))
+    valu(f"v_lshrrev_b32 v{T}, 2, v{HH}")                           # 8 h
+    valu(f"v_add3_u32 v{T}, %[dqd], v{T}, v{TT}")
+    lds(f"ds_read_b64 v[{C}:{C + 1}], v{T} offset:16384", tag + ("c",))
+    wait(tag + ("s",))
+    valu(f"v_lshlrev_b32 v{SC}, 23, v{SC}")
+    wait(tag + ("c",))
+    valu(f"v_lshlrev_b32 v{T2}, 1, v{HH}")                          # 64 h
+    valu(f"v_xor_b32 v{T2}, v{T2}, v{TT}")
+    valu(f"v_xor_b32 v{T2}, %[dqg], v{T2}")
+    valu(f"v_lshl_add_u32 v{T2}, v{HH}, 4, v{T2}")                  # + 512 h
+    valu(f"v_add_u32 v{T2}, %[dqf], v{T2}")
+    convert_half(f"v{T2}", 32768)
+    return prog
+
+
 def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
-              tail_chains: int = 2, dq: bool = False):
+              tail_chains: int = 2, dq: bool = False, dqmx: bool = False):
     reads = {}
     kops, vops = [], []
     if qk:
@@ -504,7 +587,7 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
     if sm:
         rings["SK"] = (1, 4)
         rings["ST"] = (1, 4)
-    if dq:
+    if dq or dqmx:
         rings["DQ"] = (1, 9)
     st = Stream(rings)
     st.emit("s_nop 2")  # operands may have just been written by VALU instructions
@@ -514,6 +597,8 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
     smp = sm_program(fp8, st.base["SK"], st.base["ST"]) if sm else []
     if dq:
         smp = smp + dq_program(st.base["DQ"])
+    if dqmx:
+        smp = smp + dq_program_mx(st.base["DQ"])
     sm_next = [0]
 
     queue = {}
@@ -711,6 +796,9 @@ STATEMENTS = (
     ("MLA_FUSED_BF16_DQ_ASM", dict(fp8=False, qk=True, pv=True, dq=True)),
     # The dequantization alone: the share of a wave with no rows to compute.
     ("MLA_DQ_FP4_ASM", dict(fp8=False, qk=False, pv=False, dq=True)),
+    # The same for a raw MXFP8 tile.
+    ("MLA_FUSED_BF16_DQMX_ASM", dict(fp8=False, qk=True, pv=True, dqmx=True)),
+    ("MLA_DQ_MX_ASM", dict(fp8=False, qk=False, pv=False, dqmx=True)),
 )
 
 
