@@ -17,8 +17,8 @@ Statements (T = BF16 or FP8):
 
   MLA_QK_T_ASM       QK (first tile of a unit)
   MLA_FUSED_BF16_ASM QK of tile t+1 and PV of tile t, plus DMA
-  MLA_FUSED_BF16_NODMA_ASM  the same without the DMA (FP4 pools)
-  MLA_FUSED_BF16_DQ_ASM  the same plus the dequantization of a raw FP4 tile
+  MLA_FUSED_BF16_DQ_ASM  the same without the DMA, plus the dequantization
+                     of a raw FP4 tile (FP4 pools: their DMA is issued outside)
   MLA_DQ_FP4_ASM     that dequantization alone (a wave with no rows)
   MLA_FUSED_BF16_DQMX_ASM, MLA_DQ_MX_ASM  the same two for a raw MXFP8 tile
   MLA_PV_T_ASM       PV (last tile of a unit)
@@ -792,7 +792,6 @@ STATEMENTS = (
     # FP4 pools: the BF16 tiles are dequantized in LDS, and the FP4 DMA is
     # issued outside the statement; the steady state dequantizes the tile
     # after next inside the statement.
-    ("MLA_FUSED_BF16_NODMA_ASM", dict(fp8=False, qk=True, pv=True)),
     ("MLA_FUSED_BF16_DQ_ASM", dict(fp8=False, qk=True, pv=True, dq=True)),
     # The dequantization alone: the share of a wave with no rows to compute.
     ("MLA_DQ_FP4_ASM", dict(fp8=False, qk=False, pv=False, dq=True)),
