@@ -83,14 +83,17 @@ def test_small_shapes(kv, q, H):
 
 @pytest.mark.parametrize("kv", KV_DTYPES)
 @pytest.mark.parametrize("q,H,splits", [(1, 8, 5), (5, 96, 9), (2, 112, 3), (5, 96, 0)])
-def test_rows_past_the_request_end(kv, q, H, splits):
+@pytest.mark.parametrize("page_size", [64, 16])
+def test_rows_past_the_request_end(kv, q, H, splits, page_size):
     # Row groups whose last waves hold no valid row (8 rows: waves 1-3 of
     # the group are empty; 480 rows: wave 3 of group 3; 224 rows: wave 3 of
     # group 1), with units of a single tile (32-token cuts of short
     # requests) and a 1-token request.  splits 0 plans for 8 compute units,
-    # so that each workgroup runs several units in a row.
+    # so that each workgroup runs several units in a row.  Page size 16
+    # takes the general-table kernels (a table load per lane and tile).
     lens = [q, 40, 95, 64 * 3 + 1, 900]
-    x = make_inputs(60 + q, lens, q, H, kv, kv_std=0.1 if kv == "bf16" else 1.0)
+    x = make_inputs(60 + q, lens, q, H, kv, kv_std=0.1 if kv == "bf16" else 1.0,
+                    page_size=page_size)
     out, lse = gpu_decode(x, force_splits=splits, num_cus=8 if splits == 0 else 0)
     check(out, lse, *oracle(x), tag=f"{kv} q{q} h{H} splits {splits} lens {lens}")
 
