@@ -344,10 +344,12 @@ def dq_program(base: int):
     %[dqd] = raw + w / 2, %[dqe] = 64 w, %[dqf] = bf16 tile + 512 w.
     Scratch: codes (2), one BF16 pair (2), scale, two addresses, 16 t, 32 h.
     """
-    # nine registers from an odd base, so that the two pairs start on even
-    # registers (as the ISA requires)
-    assert base % 2 == 1
-    SC, C, O, T, T2, TT, HH = base, base + 1, base + 3, base + 5, base + 6, base + 7, base + 8
+    # nine registers; the two pairs start on even registers (as the ISA
+    # requires), wherever the ring begins
+    if base % 2:
+        SC, C, O, T, T2, TT, HH = base, base + 1, base + 3, base + 5, base + 6, base + 7, base + 8
+    else:
+        C, O, SC, T, T2, TT, HH = base, base + 2, base + 4, base + 5, base + 6, base + 7, base + 8
     prog = []
 
     def valu(text):
