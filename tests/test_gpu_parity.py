@@ -251,6 +251,29 @@ def test_sweep_batch1_200k():
     check(out, lse, *oracle(x), tag="sweep 1x200k q5 h96 fp8")
 
 
+def test_sweep_batch24_200k_sampled():
+    """The largest fixed sweep batch (24 x 200k, q5, h96, FP8) at full size, in
+    the plan the sweep times; the last request is checked against the oracle."""
+    x = config_inputs(5, device=DEV, batch=24)
+    out, lse = gpu_decode(x)
+    reqs = [23]
+    o_ref, l_ref = oracle(x, reqs=reqs)
+    check(out[reqs], lse[reqs], o_ref, l_ref, tag="sweep 24x200k q5 h96 fp8 (request 23)")
+
+
+def test_sweep_ragged64_sampled():
+    """The ragged 64-request sweep batch (contexts log-uniform in [1024, 400000],
+    4.4M tokens) at full size, in the plan the sweep times.  Five requests are
+    checked against the oracle, from the shortest (1031 tokens) to the longest
+    (398038 tokens, the largest context of any workload here)."""
+    x = config_inputs(5, device=DEV, ragged=True)
+    out, lse = gpu_decode(x)
+    reqs = [31, 38, 63, 58, 9]
+    assert list(np.asarray(x.seq_lens)[reqs]) == [1031, 2492, 46931, 85484, 398038]
+    o_ref, l_ref = oracle(x, reqs=reqs)
+    check(out[reqs], lse[reqs], o_ref, l_ref, tag="sweep ragged64 q5 h96 fp8 (5 requests)")
+
+
 def test_fp8_every_code_decodes_exactly():
     # One visible token and q_len 1: the softmax weight is 1 (up to one fp32
     # rounding in the exponent), so O is that token's value row, which holds
