@@ -245,6 +245,31 @@ def test_dcp_shard_workload_sampled():
     check(out[reqs], lse[reqs], o_ref, l_ref, tag="dcp8 shard 3, 128x12500 (requests 0, 77, 127)")
 
 
+def test_dcp8_all_shards_and_combine_sampled():
+    """All 8 shards of the dcp8 workload (128 x 12500-token shards, q5, h96, FP8)
+    at full size, each in the plan bench.py times, then mla_lse_combine over
+    all 61440 rows of the 8 parts.  Three requests are checked: each shard's
+    oracle result, merged by the oracle's combine (its equality with
+    full-context attention is pinned on the CPU)."""
+    reqs = [0, 64, 127]
+    parts_o, parts_l, ref_o, ref_l = [], [], [], []
+    for r in range(8):
+        x = config_inputs(4, device=DEV, dcp_rank=r)
+        out, lse = gpu_decode(x)
+        o_r, l_r = oracle(x, reqs=reqs)
+        check(out[reqs], lse[reqs], o_r, l_r, tag=f"dcp8 shard {r} (requests 0, 64, 127)")
+        parts_o.append(out)
+        parts_l.append(lse)
+        ref_o.append(o_r)
+        ref_l.append(l_r)
+        del x
+    mo, ml = mla.lse_combine(torch.stack(parts_o).contiguous(), torch.stack(parts_l).contiguous())
+    torch.cuda.synchronize()
+    assert mo.shape == parts_o[0].shape and ml.shape == parts_l[0].shape
+    o_ref, l_ref = lse_combine_ref(np.stack(ref_o), np.stack(ref_l))
+    check(mo[reqs], ml[reqs], o_ref, l_ref, tag="dcp8 8-shard combine (requests 0, 64, 127)")
+
+
 def test_sweep_batch1_200k():
     x = config_inputs(5, device=DEV, batch=1)
     out, lse = gpu_decode(x)
