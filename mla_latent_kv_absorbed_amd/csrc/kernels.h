@@ -29,9 +29,10 @@ struct DecodeArgs {
 
 hipError_t launch_decode(int kv, bool paged, int grid, const DecodeArgs& args,
                          hipStream_t stream);
+// max_parts: the largest part count of any split request in the plan.
 hipError_t launch_merge_split(const uint8_t* plan_dev, int num_split_reqs, int rows,
-                              const float* ws_o, const float* ws_lse, float* out, float* lse,
-                              hipStream_t stream);
+                              int max_parts, const float* ws_o, const float* ws_lse, float* out,
+                              float* lse, hipStream_t stream);
 hipError_t launch_lse_combine(const float* part_o, const float* part_lse, int nparts,
                               int64_t rows, float* out, float* lse, hipStream_t stream);
 

@@ -482,8 +482,15 @@ mla_status mla_decode_merge(const void* plan_host, const void* plan_device, cons
   const float* ws_o = static_cast<const float*>(workspace);
   const float* ws_lse = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) +
                                                        h->ws_lse_offset);
+  const uint8_t* blob = static_cast<const uint8_t*>(plan_host);
+  const ReqParts* reqs = reinterpret_cast<const ReqParts*>(blob + h->off_reqs);
+  const int32_t* split = reinterpret_cast<const int32_t*>(blob + h->off_split);
+  int max_parts = 0;
+  for (int i = 0; i < h->num_split_reqs; ++i)
+    max_parts = reqs[split[i]].num_parts > max_parts ? reqs[split[i]].num_parts : max_parts;
   if (launch_merge_split(static_cast<const uint8_t*>(plan_device), h->num_split_reqs, h->rows,
-                         ws_o, ws_lse, out, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
+                         max_parts, ws_o, ws_lse, out, lse,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }
