@@ -37,17 +37,31 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 (e4m3) MFMA, vendor figure
 def mfma_peak_tflops(kv_dtype: str) -> float:
     """MFMA peak that prices the decode kernel's algorithmic FLOPs.
 
-    Each contraction takes the peak of the type it runs in.  BF16 KV: both
-    products on bf16 MFMAs.  FP8 KV: the c_kv parts of Q.K and P.V (2 * 512
-    + 2 * 512 of the 2176 FLOP per row and token) run on e4m3 MFMAs, the
-    RoPE part (2 * 64) on bf16 MFMAs, so the floor is the sum of the two
-    times and the effective peak 2176 / (2048 / 5000 + 128 / 2500).  FP4 KV:
-    the rows are dequantized exactly to BF16 and both products run on bf16
-    MFMAs; the same for MXFP8 KV.
+    BF16 KV: the bf16 dense peak (2.5 PFLOP/s).  FP8, FP4 and MXFP8 KV: the
+    e4m3 dense peak (5.0 PFLOP/s), the rate of the scaled f8f6f4 MFMA that
+    takes these stored codes as operands (an FP4 key against a query that is
+    not FP4 runs at the FP8 rate).  Whatever the kernel does to keep the
+    products exact (two e4m3 terms per query and probability, or widening to
+    BF16) is charged to the kernel, not to the peak.
     """
-    if kv_dtype in ("bf16", "fp4", "mxfp8"):
-        return MFMA_BF16_PEAK_TFLOPS
-    return 2176.0 / (2048.0 / MFMA_FP8_PEAK_TFLOPS + 128.0 / MFMA_BF16_PEAK_TFLOPS)
+    return MFMA_BF16_PEAK_TFLOPS if kv_dtype == "bf16" else MFMA_FP8_PEAK_TFLOPS
+
+
+def measured_hbm_peak():
+    """The HBM read rate measured on an MI355X by bench.py --hbm-peak, from
+    profiles/hbm_peak.txt (TB/s), or None when that summary is missing."""
+    path = os.path.join(ROOT, "profiles", "hbm_peak.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("read_tb_per_s:"):
+            try:
+                return float(line.split(":", 1)[1])
+            except ValueError:
+                return None
+    return None
+
+
 B200_CONTEXT_US = {"mtp": 1240.0, "dcp8": 826.0}  # the pages' numbers (other hardware)
 
 WORKLOADS = {
@@ -58,6 +72,7 @@ WORKLOADS = {
     "mtp-fp4": 6,   # the mtp shape over an FP4 pool
     "standard-fp4": 7,  # the standard shape over an FP4 pool
     "mtp-mxfp8": 8,  # the mtp shape over an MXFP8 pool
+    "mtp-q1": 9,    # the mtp shape at q_len 1 (one query row per head): HBM bound
 }
 
 
@@ -203,7 +218,14 @@ def run_prepare(args, dev):
 
 
 def cpu_baseline(x, max_requests: int, budget_s: float):
-    """Time the float64 oracle on a bounded sample of requests, scale to the layer."""
+    """Time the float64 oracle on a bounded sample of requests, scale to the layer.
+
+    The pool, its scales and the table are copied to host memory once,
+    untimed; each sampled request is then one oracle call on the whole pool
+    and its own table row, so the timed region holds the oracle's page-table
+    gather, its exact dequantization, the score matmul, the softmax and the
+    value sum.
+    """
     import torch
     from oracle import mla_decode_ref
     try:
@@ -211,24 +233,13 @@ def cpu_baseline(x, max_requests: int, budget_s: float):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
-    table = x.req_to_token
+    nb = x.numpy_bits()
     done, t_total = 0, 0.0
     for b in range(min(max_requests, x.batch)):
-        n = int(x.local_lens[b])
-        slots = table[b, :n].long()
-        pool = x.pool[slots].cpu()
-        sc = None if x.kv_scale is None else x.kv_scale[slots].cpu().numpy()
-        nb = dict(
-            q_nope=x.q_nope[b:b + 1].cpu().view(torch.int16).numpy().view(np.uint16),
-            q_rope=x.q_rope[b:b + 1].cpu().view(torch.int16).numpy().view(np.uint16),
-            pool=(pool.view(torch.int16).numpy().view(np.uint16) if x.kv_dtype == "bf16"
-                  else pool.numpy()),
-        )
-        compact_table = np.arange(n, dtype=np.int32)[None, :]
         t0 = time.perf_counter()
-        mla_decode_ref(nb["q_nope"], nb["q_rope"], nb["pool"], sc, compact_table,
-                       np.asarray(x.seq_lens[b:b + 1]), x.q_len, x.softmax_scale, x.kv_dtype,
-                       x.dcp_size, x.dcp_rank)
+        mla_decode_ref(nb["q_nope"][b:b + 1], nb["q_rope"][b:b + 1], nb["pool"], nb["kv_scale"],
+                       nb["req_to_token"][b:b + 1], nb["seq_lens"][b:b + 1], x.q_len,
+                       x.softmax_scale, x.kv_dtype, x.dcp_size, x.dcp_rank)
         t_total += time.perf_counter() - t0
         done += 1
         log(f"  oracle request {b}: {t_total:.1f}s so far")
@@ -237,7 +248,8 @@ def cpu_baseline(x, max_requests: int, budget_s: float):
     per_layer_us = t_total / done * x.batch * 1e6
     return {"value": per_layer_us, "unit": "us/layer", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} of {x.batch} requests of the same workload (float64 numpy "
-                      f"oracle, gather + exact dequant + matmul + softmax), scaled by "
+                      f"oracle on the host copy of the whole pool: table gather + exact "
+                      f"dequant + matmul + softmax + value sum, all timed), scaled by "
                       f"{x.batch}/{done}"}
 
 
@@ -454,6 +466,66 @@ def run_dcp_full(args, dev):
         "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
+def run_hbm_peak(args, dev):
+    """HBM ceiling measured on this GPU with plain streaming kernels.
+
+    Buffers of 4 GiB (16x the 256 MB MALL, so no cache holds them).  read:
+    libmla_probe's streaming read (each lane keeps eight 16-byte loads in
+    flight; 4 GiB read).  copy: its streaming copy (4 GiB read + 4 GiB
+    written).  write: torch's fill (4 GiB written).  Each is timed with HIP
+    events on the launch stream, median of `steps` runs after `warmup`.  The
+    read rate is the ceiling of the decode kernel, whose HBM traffic is
+    almost all reads.
+    """
+    import ctypes
+    import torch
+    probe = ctypes.CDLL(os.path.join(ROOT, "mla_latent_kv_absorbed_amd", "libmla_probe.so"))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    probe.mla_probe_read.argtypes = [vp, i64, vp, i32, vp]
+    probe.mla_probe_copy.argtypes = [vp, vp, i64, i32, vp]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes = 4 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(2048 * cus, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = int(stream.cuda_stream)
+
+    def read():
+        if probe.mla_probe_read(src.data_ptr(), nbytes, sink.data_ptr(), cus, sp) != 0:
+            raise RuntimeError("mla_probe_read failed")
+
+    def copy():
+        if probe.mla_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, cus, sp) != 0:
+            raise RuntimeError("mla_probe_copy failed")
+
+    kinds = {"read": (read, nbytes), "write": (lambda: dst.fill_(2.0), nbytes),
+             "copy": (copy, 2 * nbytes)}
+    rows = {}
+    for name, (fn, moved) in kinds.items():
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+        med = float(np.median(us))
+        rows[name] = {"bytes": moved, "us_median": round(med, 1),
+                      "tb_per_s": round(moved / (med * 1e-6) / 1e12, 3),
+                      "tb_per_s_best": round(moved / (float(us.min()) * 1e-6) / 1e12, 3)}
+        log(f"  {name}: {rows[name]['tb_per_s']} TB/s")
+    if not torch.equal(dst, src):
+        raise RuntimeError("probe copy mismatch")
+    print(json.dumps({"hbm_peak": rows, "vendor_tb_per_s": HBM_PEAK_TBPS,
+                      "read_frac_of_vendor": round(rows["read"]["tb_per_s"] / HBM_PEAK_TBPS, 4),
+                      "buffers_gib": 4, "compute_units": cus, "steps": args.steps,
+                      "warmup": args.warmup}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -481,6 +553,9 @@ def main():
                     help="instead of the one-line step benchmark: time mla_prepare (Q "
                          "absorption, RoPE, KV append) on the prepare workloads and print one "
                          "JSON object")
+    ap.add_argument("--hbm-peak", action="store_true",
+                    help="instead of the one-line step benchmark: measure this GPU's HBM read, "
+                         "write and copy rates with plain streaming kernels over 4 GiB buffers")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before the warmup, run one plain device copy of this many MB (for "
                          "scaling HBM counters); not timed")
@@ -504,6 +579,9 @@ def main():
         return
     if args.prepare:
         run_prepare(args, dev)
+        return
+    if args.hbm_peak:
+        run_hbm_peak(args, dev)
         return
     cfg = WORKLOADS[args.workload]
     log(f"generating inputs for {CONFIGS[cfg]['name']} on {dev}")
@@ -583,12 +661,16 @@ def main():
         "traffic": traffic, "kernel": "mla::decode_kernel", "kernel_us": round(k_us, 2),
         "flops_per_launch": flops, "algorithmic_bytes_per_launch": all_bytes,
     }
-    if x.q_len == 1 and x.kv_dtype == "bf16" and x.num_heads <= 128:
-        # Below the bf16 ridge (about 312 FLOP/B): HBM bound.
+    # The bound is whichever floor is longer at the vendor peaks: MFMA time
+    # of the algorithmic FLOPs, or HBM time of the algorithmic bytes.
+    t_mfma_floor = flops / (peak * 1e12)
+    t_hbm_floor = all_bytes / (HBM_PEAK_TBPS * 1e12)
+    if t_hbm_floor > t_mfma_floor:
         bw = all_bytes / (k_us * 1e-6) / 1e12
         roofline.update({"bound": "hbm", "achieved": round(bw * 1e3, 1),
                          "peak": HBM_PEAK_TBPS * 1e3, "unit": "GB/s",
                          "frac": round(bw / HBM_PEAK_TBPS, 4)})
+    hbm_meas = measured_hbm_peak()
 
     result = {
         "metric": METRIC,
@@ -609,6 +691,9 @@ def main():
                    "kv": x.kv_dtype, "page_size": x.page_size, "dcp": [x.dcp_size, x.dcp_rank]},
         "kv_tb_per_s": round(kv_tbps, 3),
         "kv_hbm_peak_frac": round(kv_tbps / HBM_PEAK_TBPS, 4),
+        "kv_hbm_measured_peak_frac": (round(kv_tbps / hbm_meas, 4) if hbm_meas else None),
+        "hbm_measured_read_peak_tb_per_s": hbm_meas,
+        "floors_us": {"mfma": round(t_mfma_floor * 1e6, 1), "hbm": round(t_hbm_floor * 1e6, 1)},
         "mfma_frac": round(tflops / peak, 4),
         "step_us_p10_p50_p90": [round(float(np.percentile(times_ms, p)) * 1e3, 2)
                                 for p in (10, 50, 90)],

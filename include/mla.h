@@ -124,6 +124,34 @@ mla_status mla_decode_plan(const mla_decode_desc* desc, const int32_t* seq_lens_
                            size_t* workspace_bytes);
 
 /*
+ * Opt-in host check of the table contract that mla_decode relies on (page
+ * "resident VRAM accounting", section "req_to_token": an int32 table maps
+ * each request's token index to a pool slot; pages are page_size
+ * consecutive slots).  mla_decode never reads the table on the host; a
+ * caller that wants the contract verified copies the table to host memory
+ * and calls this before decoding.
+ *
+ *   desc:              the description the plan is made from (batch,
+ *                      q_len, page_size, dcp_size, dcp_rank are used).
+ *   seq_lens_host:     int32 [B] global lengths, host memory.
+ *   req_to_token_host: int32 [B, stride] host copy of the table.
+ *   stride:            its row stride in entries (>= every local length).
+ *   num_slots:         the pool's slot count.
+ *
+ * For every request b and local index j < n_b (n_b = the number of
+ * positions p < L_b with p % W == r) it checks 0 <= table[b, j] < num_slots
+ * and, when page_size is a multiple of 32, table[b, j] = table[b, j - j % 32]
+ * + j % 32 (the 32 slots behind each entry the kernel reads are
+ * consecutive).  Entries past n_b are not read by mla_decode and not checked.
+ * Returns MLA_OK; MLA_ERR_INVALID_ARG for bad arguments or a broken contract,
+ * with *bad_request / *bad_index (if not NULL) set to the first failing
+ * entry (-1 / -1 for an argument error); nothing else is written.
+ */
+mla_status mla_check_table(const mla_decode_desc* desc, const int32_t* seq_lens_host,
+                           const int32_t* req_to_token_host, int64_t stride, int64_t num_slots,
+                           int64_t* bad_request, int64_t* bad_index);
+
+/*
  * Absorbed MLA decode (DP16-vs-DP2 page, section "MLA": the kernel that
  * scores heads x q_len rows against the latent KV, called attn_mqa there).
  *

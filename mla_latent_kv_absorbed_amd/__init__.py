@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     KV_MXFP8,
     DecodeDesc,
     MlaError,
+    check_table,
     Plan,
     decode,
     library_path,

@@ -62,6 +62,9 @@ def load_library():
     lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, sz,
                                     ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.mla_decode_plan.restype = i32
+    lib.mla_check_table.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, i64, i64,
+                                    ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.mla_check_table.restype = i32
     lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, i64, vp, ctypes.c_float,
                                vp, sz, vp, vp, vp]
     lib.mla_decode.restype = i32
@@ -172,6 +175,27 @@ def make_plan(desc: DecodeDesc, seq_lens, device=None) -> Plan:
     return p
 
 
+def check_table(desc: DecodeDesc, seq_lens, req_to_token, num_slots: int) -> None:
+    """mla_check_table on a host copy of the table: raises MlaError naming the
+    first entry that is out of the pool or breaks the 32-slot runs a paged
+    plan relies on."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    if lens.shape != (desc.batch,):
+        raise MlaError(f"seq_lens must have {desc.batch} entries")
+    if hasattr(req_to_token, "cpu"):
+        req_to_token = req_to_token.cpu().numpy()
+    table = np.ascontiguousarray(np.asarray(req_to_token, dtype=np.int32))
+    if table.ndim != 2 or table.shape[0] != desc.batch:
+        raise MlaError("req_to_token must be [batch, stride]")
+    bad_b, bad_j = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = load_library().mla_check_table(ctypes.byref(desc), lens.ctypes.data,
+                                        table.ctypes.data, int(table.shape[1]), int(num_slots),
+                                        ctypes.byref(bad_b), ctypes.byref(bad_j))
+    if st != MLA_OK:
+        where = "" if bad_b.value < 0 else f" at request {bad_b.value}, index {bad_j.value}"
+        raise MlaError(f"req_to_token breaks the table contract{where}", st)
+
+
 def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
 
@@ -185,11 +209,13 @@ def _stream(stream) -> int:
 
 def decode(plan: Plan, q_nope, q_rope, kv_pool, kv_scale, req_to_token, seq_lens,
            softmax_scale: float, workspace=None, out=None, lse=None, stream=None,
-           phase: str = "both"):
+           phase: str = "both", verify_table: bool = False):
     """mla_decode on torch device tensors; allocates out / lse / workspace if not given.
 
     phase "attend" runs only mla_decode_attend, "merge" only mla_decode_merge
     (same arguments; the workspace must then be the one the attend call used).
+    verify_table copies req_to_token and seq_lens to the host first and runs
+    mla_check_table on them (a synchronizing debug check).
     """
     if phase not in ("both", "attend", "merge"):
         raise MlaError(f"unknown phase {phase!r}")
@@ -225,13 +251,28 @@ def decode(plan: Plan, q_nope, q_rope, kv_pool, kv_scale, req_to_token, seq_lens
         raise MlaError("req_to_token and seq_lens must be int32")
     if req_to_token.dim() != 2 or req_to_token.shape[0] != B:
         raise MlaError("req_to_token must be [batch, stride]")
+    if seq_lens.dim() != 1 or seq_lens.numel() != B:
+        raise MlaError(f"seq_lens must hold {B} entries")
+    o_shape = (B, h["q_len"], h["num_heads"], 512)
     if out is None:
-        out = torch.empty((B, h["q_len"], h["num_heads"], 512), dtype=torch.float32, device=dev)
+        out = torch.empty(o_shape, dtype=torch.float32, device=dev)
+    elif out.dtype != torch.float32 or tuple(out.shape) != o_shape or out.device != dev or \
+            not out.is_contiguous():
+        raise MlaError(f"out must be a contiguous float32 {list(o_shape)} tensor on {dev}")
     if lse is None:
-        lse = torch.empty((B, h["q_len"], h["num_heads"]), dtype=torch.float32, device=dev)
+        lse = torch.empty(o_shape[:3], dtype=torch.float32, device=dev)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != o_shape[:3] or lse.device != dev or \
+            not lse.is_contiguous():
+        raise MlaError(f"lse must be a contiguous float32 {list(o_shape[:3])} tensor on {dev}")
     ws_bytes = h["workspace_bytes"]
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    elif workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != dev or
+                                    not workspace.is_contiguous()):
+        raise MlaError(f"workspace must be a contiguous uint8 tensor on {dev}")
+    if verify_table:
+        check_table(plan.desc, seq_lens.cpu().numpy(), req_to_token.cpu().numpy(),
+                    int(kv_pool.shape[0]))
     ws_given = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     lib = load_library()
     if phase == "merge":

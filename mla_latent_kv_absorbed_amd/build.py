@@ -25,16 +25,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build_library(verbose: bool = False) -> str:
-    out = os.path.join(HERE, "libmla.so")
+# The HBM probe kernels that bench.py --hbm-peak times (not part of libmla).
+PROBE_SOURCES = [os.path.join(HERE, "csrc", "hbm_probe.hip")]
+
+
+def _build(sources, name: str, verbose: bool) -> str:
+    out = os.path.join(HERE, name)
     tmp = out + f".tmp{os.getpid()}"
-    cmd = [hipcc()] + HIPCC_FLAGS + SOURCES + ["-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + sources + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("libmla build failed:\n" + res.stdout + res.stderr)
+        raise RuntimeError(f"{name} build failed:\n" + res.stdout + res.stderr)
     if verbose:
         print(" ".join(cmd))
     os.replace(tmp, out)
+    return out
+
+
+def build_library(verbose: bool = False) -> str:
+    """Builds libmla.so (and the probe library libmla_probe.so); returns libmla's path."""
+    out = _build(SOURCES, "libmla.so", verbose)
+    _build(PROBE_SOURCES, "libmla_probe.so", verbose)
     return out
 
 

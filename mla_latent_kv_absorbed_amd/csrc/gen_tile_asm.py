@@ -803,7 +803,8 @@ STATEMENTS = (
 )
 
 
-def main() -> None:
+def generate() -> str:
+    """The text of tile_asm.inc."""
     out = ["// Generated by gen_tile_asm.py -- do not edit.\n"]
     lines, low = rescale_statement()
     out.append(emit_macro("MLA_RESCALE_ASM", lines))
@@ -814,9 +815,13 @@ def main() -> None:
         out.append(emit_macro(name, lines))
         regs = ", ".join(f'"v{r}"' for r in range(low, SCRATCH_HI + 1))
         out.append(f"// Scratch registers of {name}.\n#define {name[:-4]}_CLOBBERS {regs}, \"memory\"\n")
+    return "\n".join(out)
+
+
+def main() -> None:
     here = os.path.dirname(os.path.abspath(__file__))
     with open(os.path.join(here, "tile_asm.inc"), "w") as f:
-        f.write("\n".join(out))
+        f.write(generate())
 
 
 if __name__ == "__main__":

@@ -394,6 +394,32 @@ mla_status mla_decode_plan(const mla_decode_desc* d, const int32_t* seq_lens_hos
   return MLA_OK;
 }
 
+mla_status mla_check_table(const mla_decode_desc* d, const int32_t* seq_lens_host,
+                           const int32_t* table, int64_t stride, int64_t num_slots,
+                           int64_t* bad_request, int64_t* bad_index) {
+  auto fail = [&](int64_t b, int64_t j) {
+    if (bad_request) *bad_request = b;
+    if (bad_index) *bad_index = j;
+    return MLA_ERR_INVALID_ARG;
+  };
+  if (check_desc(d) != MLA_OK || !seq_lens_host || !table || num_slots < 1 || stride < 1)
+    return fail(-1, -1);
+  const bool runs = d->page_size % kTile == 0;
+  for (int b = 0; b < d->batch; ++b) {
+    const int64_t L = seq_lens_host[b];
+    if (L < d->q_len) return fail(-1, -1);
+    const int64_t n = local_len(L, d->dcp_size, d->dcp_rank);
+    if (n > stride) return fail(-1, -1);
+    const int32_t* row = table + (int64_t)b * stride;
+    for (int64_t j = 0; j < n; ++j) {
+      const int64_t s = row[j];
+      if (s < 0 || s >= num_slots) return fail(b, j);
+      if (runs && s != (int64_t)row[j - j % kTile] + j % kTile) return fail(b, j);
+    }
+  }
+  return MLA_OK;
+}
+
 }  // extern "C"
 
 namespace {

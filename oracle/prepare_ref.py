@@ -35,13 +35,15 @@ Readings where the pages are silent:
   value), so the stored bytes are compared bit for bit.
 
 Where floating point decides a stored code (the FP8 bytes, the BF16 bits of
-the roped values), this oracle takes each float32 step in the order the GPU
-kernel takes it, so that the codes can be compared bit for bit: RoPE as
-y0 = x0 c - x1 s, y1 = x0 s + x1 c with every product and sum rounded to
-float32 (no fused multiply-add), then round-to-nearest-even to BF16; the
-scale and the quotient x / scale as correctly rounded float32 divisions.
-The absorbed query, a sum of 128 products, is computed in float64 and
-compared within one BF16 unit in the last place.
+the roped values), the stored code is defined by float32 arithmetic, so that
+codes can be compared bit for bit: RoPE is y0 = x0 c - x1 s, y1 = x0 s + x1 c
+with every product and every sum a correctly rounded float32 operation (no
+fused multiply-add), then round-to-nearest-even to BF16; the FP8 scale and
+the quotient x / scale are correctly rounded float32 divisions.  This is the
+definition the library header states for mla_prepare; rope_f32 is pinned to
+it bit for bit by a test that evaluates every product and sum from exact
+rationals.  The absorbed query, a sum of 128 products, is computed in
+float64 and compared within one BF16 unit in the last place.
 """
 
 from __future__ import annotations

@@ -103,8 +103,6 @@ def test_rows_past_the_request_end(kv, q, H, splits, page_size):
 @pytest.mark.parametrize("q", [1, 5])
 @pytest.mark.parametrize("splits", [1, 2, 7, 40])
 def test_peaked_variants_and_forced_splits(kv, variant, q, splits):
-    if kv in ("fp4", "mxfp8") and variant == "planted":
-        pytest.skip("the planted variant is defined for BF16 and FP8 pools only")
     x = make_inputs(50, [1300, 257], q, 32, kv, variant=variant,
                     kv_std=0.1 if kv == "bf16" else 1.0)
     out, lse = gpu_decode(x, force_splits=splits)
@@ -230,11 +228,38 @@ def test_standard_workload_full():
 
 
 def test_mtp_100k_workload_sampled():
+    """The mtp workload in the plan bench.py times: requests 0 and 11 against the
+    oracle, and all 16 requests against a run of the same inputs with every
+    request in one piece (no split, no merge)."""
     x = config_inputs(3, device=DEV)
     out, lse = gpu_decode(x)
     reqs = [0, 11]
     o_ref, l_ref = oracle(x, reqs=reqs)
     check(out[reqs], lse[reqs], o_ref, l_ref, tag="mtp 16x100k q5 h96 fp8 (requests 0, 11)")
+    o1, l1 = gpu_decode(x, force_splits=1)
+    check(out, lse, o1.double().cpu().numpy(), l1.double().cpu().numpy(),
+          tag="mtp 16x100k: planner cuts vs unsplit, all 16 requests")
+
+
+@pytest.mark.parametrize("variant", ["planted", "qx30"])
+def test_mtp_100k_peaked_sampled(variant):
+    """The mtp shape (16 x 100k, q5, h96, FP8) at full size with a peaked score
+    distribution, in the plan bench.py times: two requests against the oracle."""
+    x = make_inputs(3, [100000] * 16, 5, 96, "fp8", device=DEV, kv_std=1.0, variant=variant)
+    out, lse = gpu_decode(x)
+    reqs = [2, 13]
+    o_ref, l_ref = oracle(x, reqs=reqs)
+    check(out[reqs], lse[reqs], o_ref, l_ref, tag=f"mtp 16x100k {variant} (requests 2, 13)")
+
+
+def test_mtp_q1_companion_sampled():
+    """The q_len 1 companion of the mtp shape (16 x 100k, 96 heads, FP8), in the
+    plan bench.py times: requests 0 and 15 against the oracle."""
+    x = config_inputs(9, device=DEV)
+    out, lse = gpu_decode(x)
+    reqs = [0, 15]
+    o_ref, l_ref = oracle(x, reqs=reqs)
+    check(out[reqs], lse[reqs], o_ref, l_ref, tag="mtp-q1 16x100k q1 h96 fp8 (requests 0, 15)")
 
 
 def test_dcp_shard_workload_sampled():
@@ -276,6 +301,18 @@ def test_sweep_batch1_200k():
     check(out, lse, *oracle(x), tag="sweep 1x200k q5 h96 fp8")
 
 
+@pytest.mark.parametrize("B", [2, 4, 8, 12, 16, 20])
+def test_sweep_batches_200k_sampled(B):
+    """Sweep batches 2..20 at 200k (q5, h96, FP8) in the plans the sweep times:
+    the last request of each against the oracle."""
+    x = config_inputs(5, device=DEV, batch=B)
+    out, lse = gpu_decode(x)
+    reqs = [B - 1]
+    o_ref, l_ref = oracle(x, reqs=reqs)
+    check(out[reqs], lse[reqs], o_ref, l_ref, tag=f"sweep {B}x200k (request {B - 1})")
+    del x
+
+
 def test_sweep_batch24_200k_sampled():
     """The largest fixed sweep batch (24 x 200k, q5, h96, FP8) at full size, in
     the plan the sweep times; the last request is checked against the oracle."""
@@ -297,6 +334,33 @@ def test_sweep_ragged64_sampled():
     assert list(np.asarray(x.seq_lens)[reqs]) == [1031, 2492, 46931, 85484, 398038]
     o_ref, l_ref = oracle(x, reqs=reqs)
     check(out[reqs], lse[reqs], o_ref, l_ref, tag="sweep ragged64 q5 h96 fp8 (5 requests)")
+
+
+@pytest.mark.parametrize("kv", KV_DTYPES)
+def test_paged_tile_at_the_end_of_a_short_pool(kv):
+    """A paged table (page size 32) whose last valid tile starts 4 slots before
+    the end of a pool that is not a multiple of 32 slots: the tile must read
+    its own slots, not slots re-based into the pool."""
+    x = make_inputs(70, [36, 40], 1, 16, kv, page_size=32, kv_std=0.1 if kv == "bf16" else 1.0)
+    # Move request 0's second page (its 4 valid tokens) to the last 4 slots of
+    # a pool cut to 100 slots more than it needs.
+    n_slots = x.num_slots
+    extra = 100 - n_slots % 32 if n_slots % 32 else 68
+    pool = torch.cat([x.pool, x.pool[:extra].clone()], 0)
+    sc = None if x.kv_scale is None else torch.cat([x.kv_scale, x.kv_scale[:extra].clone()], 0)
+    end = pool.shape[0]
+    assert end % 32 != 0
+    table = x.req_to_token.clone()
+    src = table[0, 32:36].long()
+    dst = torch.arange(end - 4, end)
+    pool[dst] = pool[src]
+    if sc is not None:
+        sc[dst] = sc[src]
+    table[0, 32:36] = dst.to(torch.int32)
+    table[0, 36:64] = 0
+    x = type(x)(**dict(x.__dict__, pool=pool, kv_scale=sc, req_to_token=table))
+    out, lse = gpu_decode(x)
+    check(out, lse, *oracle(x), tag=f"{kv} paged tile at the end of a {end}-slot pool")
 
 
 def test_fp8_every_code_decodes_exactly():

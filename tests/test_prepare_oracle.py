@@ -136,6 +136,58 @@ def test_rope_is_a_complex_rotation():
     np.testing.assert_allclose(y[:, 1::2], z.imag, rtol=0, atol=2e-6)
 
 
+def _round_f32(q):
+    """Nearest float32 (ties to even) of an exact rational q, by integer
+    arithmetic: an independent statement of a correctly rounded float32
+    operation."""
+    from fractions import Fraction
+    if q == 0:
+        return 0.0
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)                       # subnormals share the smallest exponent
+    scaled = a / Fraction(2) ** (e - 23)   # mantissa with 23 fraction bits
+    m = scaled.numerator // scaled.denominator
+    rem = scaled - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    return sign * float(Fraction(m) * Fraction(2) ** (e - 23))
+
+
+def test_rope_bits_match_exact_rational_rounding():
+    """Every output bit of rope_f32 against the definition: each product
+    x0 c, x1 s, x0 s, x1 c correctly rounded to float32, then the difference
+    / sum of the rounded products correctly rounded to float32 (no fused
+    multiply-add), with each rounding computed from exact rationals."""
+    from fractions import Fraction
+    rng = _rng(41)
+    n = 300
+    x = rng.standard_normal((n, 2)).astype(np.float32) * np.float32(3.0)
+    th = rng.uniform(-50, 50, n)
+    c, s = np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
+    # Cases where the two products nearly cancel (the difference is exact in
+    # float32 but not in a wider rounding of the operands), and tiny values.
+    x[:40, 1] = (x[:40, 0] * c[:40] / np.where(s[:40] == 0, 1, s[:40])).astype(np.float32)
+    x[40:60] *= np.float32(1e-30)
+    xx = np.zeros((n, 64), np.float32)
+    xx[:, 0:2] = x
+    cc = np.zeros((n, 32), np.float32)
+    ss = np.zeros((n, 32), np.float32)
+    cc[:, 0], ss[:, 0] = c, s
+    y = P.rope_f32(xx, cc, ss)
+    for k in range(n):
+        F = [Fraction(float(v)) for v in (x[k, 0], x[k, 1], c[k], s[k])]
+        p0c, p1s = _round_f32(F[0] * F[2]), _round_f32(F[1] * F[3])
+        p0s, p1c = _round_f32(F[0] * F[3]), _round_f32(F[1] * F[2])
+        y0 = np.float32(_round_f32(Fraction(p0c) - Fraction(p1s)))
+        y1 = np.float32(_round_f32(Fraction(p0s) + Fraction(p1c)))
+        assert y[k, 0].view(np.uint32) == y0.view(np.uint32), k
+        assert y[k, 1].view(np.uint32) == y1.view(np.uint32), k
+
+
 def test_q_rope_uses_each_tokens_position():
     rng = _rng(5)
     T, H = 4, 3

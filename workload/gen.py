@@ -274,8 +274,6 @@ def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str
         else:
             pool[:, D_C] = 0x7E  # e4m3fn 448
     elif variant == "planted":
-        if kv_dtype in ("fp4", "mxfp8"):
-            raise ValueError("the planted variant is defined for BF16 and FP8 pools")
         rng = _np_rng(cfg_id, _T_PLANT, extra)
         q0 = torch.cat([qn[:, 0, 0].float(), qr[:, 0, 0].float()], dim=-1).cpu()  # [B, 576]
         for b in range(B):
@@ -287,6 +285,10 @@ def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str
             if kv_dtype == "bf16":
                 vals = (direction * 40.0).to(torch.bfloat16)
                 pool[slots.to(device)] = vals.to(device).expand(len(js), D_K)
+            elif kv_dtype in ("fp4", "mxfp8"):
+                enc = _encode_fp4_row if kv_dtype == "fp4" else _encode_mxfp8_row
+                row = torch.from_numpy(enc(direction.numpy().astype(np.float64) * 40.0))
+                pool[slots.to(device)] = row.to(device).expand(len(js), row.numel())
             else:
                 sc = kv_scale[slots.to(device)].cpu()
                 vals = (direction[None, :] * 40.0 / sc[:, None]).clamp(-448, 448)
@@ -300,6 +302,60 @@ def make_inputs(cfg_id: int, seq_lens, q_len: int, num_heads: int, kv_dtype: str
         kv_scale=kv_scale, req_to_token=torch.from_numpy(table).to(device),
         softmax_scale=softmax_scale_default(), dcp_size=dcp_size, dcp_rank=dcp_rank,
         name=name, meta=dict(cfg_id=cfg_id, variant=variant))
+
+
+# e2m1 magnitudes by code (0..7); code | 8 is the negative value.
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _block_exponent(amax: float, top: float) -> int:
+    """Smallest e in [-64, 64] with amax <= top * 2^e (-64 for amax = 0)."""
+    if amax == 0.0:
+        return -64
+    e = int(math.ceil(math.log2(amax / top)))
+    while amax > top * 2.0 ** e:
+        e += 1
+    while e > -64 and amax <= top * 2.0 ** (e - 1):
+        e -= 1
+    return max(-64, min(64, e))
+
+
+def _encode_fp4_row(v: np.ndarray) -> np.ndarray:
+    """One FP4 row (336 bytes) holding the 576 values v: per 16-element block
+    a power-of-two scale 2^e (byte 127 + e) and e2m1 codes of v / 2^e, each
+    the nearest magnitude (ties to the even code), so that the stored row is
+    a close copy of v.  Input construction only: the decode path and the
+    oracle read whatever bytes are stored."""
+    out = np.zeros(FP4_ROW_BYTES, dtype=np.uint8)
+    codes = np.zeros(D_K, dtype=np.uint8)
+    for k in range(D_K // 16):
+        blk = v[16 * k:16 * k + 16]
+        e = _block_exponent(float(np.abs(blk).max()), 6.0)
+        out[FP4_CODE_BYTES + k] = 127 + e
+        mag = np.minimum(np.abs(blk) / 2.0 ** e, 6.0)
+        d = np.abs(mag[:, None] - _E2M1[None, :])
+        best = d.min(axis=1, keepdims=True)
+        ties = np.isclose(d, best, rtol=0.0, atol=0.0)
+        # among the nearest codes prefer the even one
+        c = np.where(ties & (np.arange(8)[None, :] % 2 == 0), np.arange(8)[None, :], 99).min(1)
+        c = np.where(c == 99, d.argmin(axis=1), c)
+        codes[16 * k:16 * k + 16] = c | np.where(blk < 0, 8, 0)
+    out[:FP4_CODE_BYTES] = codes[0::2] | (codes[1::2] << 4)
+    return out
+
+
+def _encode_mxfp8_row(v: np.ndarray) -> np.ndarray:
+    """One MXFP8 row (608 bytes) holding the 576 values v: per 32-element
+    block a power-of-two scale 2^e (byte 127 + e) and e4m3fn codes of v / 2^e
+    rounded to nearest even (torch's conversion).  Input construction only."""
+    out = np.zeros(MXFP8_ROW_BYTES, dtype=np.uint8)
+    for k in range(D_K // 32):
+        blk = v[32 * k:32 * k + 32]
+        e = _block_exponent(float(np.abs(blk).max()), 448.0)
+        out[D_K + k] = 127 + e
+        q = torch.from_numpy((blk / 2.0 ** e).astype(np.float32)).to(torch.float8_e4m3fn)
+        out[32 * k:32 * k + 32] = q.view(torch.uint8).numpy()
+    return out
 
 
 def _poison(pool, kv_scale, unused, kv_dtype: str) -> None:
@@ -354,8 +410,9 @@ def shard_from_full(full: DecodeInputs, dcp_size: int, dcp_rank: int,
         dcp_size=W, dcp_rank=r, name=f"{full.name}/shard{r}", meta=dict(full.meta, shard=r))
 
 
-# The five workloads, and companions of the same shapes over FP4 pools (6, 7)
-# and an MXFP8 pool (8).
+# The five workloads, companions of the same shapes over FP4 pools (6, 7) and
+# an MXFP8 pool (8), and the mtp shape at q_len 1 (9: 96 query rows per
+# request, below the e4m3 ridge, so bound by HBM rather than by the MFMAs).
 # Each is a decode call (or, for DCP, eight shard calls and one merge) on one
 # GPU.
 CONFIGS = {
@@ -375,6 +432,8 @@ CONFIGS = {
             num_heads=128, kv_dtype="fp4"),
     8: dict(name="mtp-16x100k-q5-h96-mxfp8", seq_lens=[100000] * 16, q_len=5, num_heads=96,
             kv_dtype="mxfp8"),
+    9: dict(name="mtp-q1-16x100k-q1-h96-fp8", seq_lens=[100000] * 16, q_len=1, num_heads=96,
+            kv_dtype="fp8"),
 }
 SWEEP_BATCHES = (1, 2, 4, 8, 12, 16, 20, 24)
 
