@@ -24,10 +24,12 @@
  * p % W == r, and its table is indexed by the local index j = (p - r) / W.
  *
  * Memory: every buffer belongs to the caller.  The library allocates no
- * device memory and keeps no mutable global state; every call is
- * asynchronous on the caller's HIP stream and thread-safe.  Argument errors
- * are detected on the host and returned synchronously; nothing is enqueued
- * when a call fails.
+ * device memory and keeps no mutable global state, with one exception that
+ * only mla_decode_noalloc uses: a fixed scratch array per GPU, held from its
+ * first use until the process ends.  Every call is asynchronous on the
+ * caller's HIP stream and thread-safe (mla_decode_noalloc: see its own note
+ * on overlapping calls).  Argument errors are detected on the host and
+ * returned synchronously; nothing is enqueued when a call fails.
  */
 #ifndef MLA_H_
 #define MLA_H_
@@ -213,6 +215,32 @@ mla_status mla_decode_attend(const void* plan_host, const void* plan_device,
 mla_status mla_decode_merge(const void* plan_host, const void* plan_device,
                             const void* workspace, size_t workspace_bytes, float* out,
                             float* lse, void* stream);
+
+/*
+ * mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call without the workspace arguments.  The split partials go to a
+ * scratch array of MLA_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on, from the first such call on that GPU until the process
+ * ends; nothing is allocated per call (no hipMalloc, hipFree or allocating
+ * library routine).
+ *
+ * Arguments, layouts and errors as for mla_decode; in addition a plan whose
+ * *workspace_bytes exceeds MLA_NOALLOC_SCRATCH_BYTES is rejected with
+ * MLA_ERR_WORKSPACE_TOO_SMALL (nothing is enqueued; mla_decode with a
+ * caller workspace handles it).  The scratch array is shared by every call
+ * on a GPU and keeps the last call's contents (the kernels write every
+ * partial before reading it, so nothing needs clearing); calls that overlap
+ * on one GPU (on different streams, or from different host threads without
+ * ordering) race on it and must not be issued.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+mla_status mla_decode_noalloc(const void* plan_host, const void* plan_device,
+                              const void* q_nope_absorbed, const void* q_rope,
+                              const void* kv_pool, const float* kv_scale, int64_t num_slots,
+                              const int32_t* req_to_token, int64_t req_to_token_stride,
+                              const int32_t* seq_lens, float softmax_scale, float* out,
+                              float* lse, void* stream);
 
 /*
  * Merge num_parts partial results by log-sum-exp (DP16-vs-DP2 page, section

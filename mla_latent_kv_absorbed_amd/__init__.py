@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     check_table,
     Plan,
     decode,
+    decode_noalloc,
     library_path,
     load_library,
     lse_combine,

@@ -70,6 +70,9 @@ def load_library():
     lib.mla_decode.restype = i32
     lib.mla_decode_attend.argtypes = lib.mla_decode.argtypes
     lib.mla_decode_attend.restype = i32
+    lib.mla_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, i64, vp,
+                                       ctypes.c_float, vp, vp, vp]
+    lib.mla_decode_noalloc.restype = i32
     lib.mla_decode_merge.argtypes = [vp, vp, vp, sz, vp, vp, vp]
     lib.mla_decode_merge.restype = i32
     lib.mla_lse_combine.argtypes = [vp, vp, i32, i64, vp, vp, vp]
@@ -287,6 +290,36 @@ def decode(plan: Plan, q_nope, q_rope, kv_pool, kv_scale, req_to_token, seq_lens
                 _stream(stream))
     if st != MLA_OK:
         raise MlaError(f"mla_decode ({phase}) failed", st)
+    return out, lse
+
+
+def decode_noalloc(plan: Plan, q_nope, q_rope, kv_pool, kv_scale, req_to_token, seq_lens,
+                   softmax_scale: float, out, lse, stream=None):
+    """mla_decode_noalloc: mla_decode with the split partials in the library's
+    per-GPU scratch array.  out / lse must be given (nothing is allocated)."""
+    import torch
+    h = plan.header
+    o_shape = (h["batch"], h["q_len"], h["num_heads"], 512)
+    for name, t, shape in (("out", out, o_shape), ("lse", lse, o_shape[:3])):
+        if t is None or t.dtype != torch.float32 or tuple(t.shape) != shape or \
+                t.device != q_nope.device or not t.is_contiguous():
+            raise MlaError(f"{name} must be a contiguous float32 {list(shape)} tensor on "
+                           f"{q_nope.device}")
+    if plan.device is None:
+        raise MlaError("plan has no device copy (call plan.to_device())")
+    fp8 = h["kv_dtype"] == KV_FP8
+    if seq_lens.numel() != h["batch"] or seq_lens.dtype != torch.int32:
+        raise MlaError(f"seq_lens must be int32 with {h['batch']} entries")
+    if req_to_token.dim() != 2 or req_to_token.shape[0] != h["batch"] or \
+            req_to_token.dtype != torch.int32:
+        raise MlaError("req_to_token must be int32 [batch, stride]")
+    st = load_library().mla_decode_noalloc(
+        plan.host.ctypes.data, _ptr(plan.device), _ptr(q_nope), _ptr(q_rope), _ptr(kv_pool),
+        _ptr(kv_scale if fp8 else None), int(kv_pool.shape[0]), _ptr(req_to_token),
+        int(req_to_token.shape[1]), _ptr(seq_lens), float(softmax_scale), _ptr(out), _ptr(lse),
+        _stream(stream))
+    if st != MLA_OK:
+        raise MlaError("mla_decode_noalloc failed", st)
     return out, lse
 
 

@@ -33,6 +33,10 @@ hipError_t launch_decode(int kv, bool paged, int grid, const DecodeArgs& args,
 hipError_t launch_merge_split(const uint8_t* plan_dev, int num_split_reqs, int rows,
                               int max_parts, const float* ws_o, const float* ws_lse, float* out,
                               float* lse, hipStream_t stream);
+// Device address of the current device's no-alloc scratch array (capacity
+// kNoAllocScratchBytes), looked up once per device with hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_lse_combine(const float* part_o, const float* part_lse, int nparts,
                               int64_t rows, float* out, float* lse, hipStream_t stream);
 

@@ -535,6 +535,22 @@ mla_status mla_decode(const void* plan_host, const void* plan_device, const void
   return mla_decode_merge(plan_host, plan_device, workspace, workspace_bytes, out, lse, stream);
 }
 
+mla_status mla_decode_noalloc(const void* plan_host, const void* plan_device, const void* q_nope,
+                              const void* q_rope, const void* kv_pool, const float* kv_scale,
+                              int64_t num_slots, const int32_t* req_to_token,
+                              int64_t req_to_token_stride, const int32_t* seq_lens,
+                              float softmax_scale, float* out, float* lse, void* stream) {
+  if (!plan_host || !aligned16(plan_host)) return MLA_ERR_INVALID_ARG;
+  const PlanHeader* h = static_cast<const PlanHeader*>(plan_host);
+  if (h->magic != kPlanMagic || h->version != kPlanVersion) return MLA_ERR_INVALID_ARG;
+  if (h->workspace_bytes > (int64_t)kNoAllocScratchBytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (h->workspace_bytes > 0 && noalloc_scratch(&ws) != hipSuccess) return MLA_ERR_HIP;
+  return mla_decode(plan_host, plan_device, q_nope, q_rope, kv_pool, kv_scale, num_slots,
+                    req_to_token, req_to_token_stride, seq_lens, softmax_scale, ws,
+                    ws ? kNoAllocScratchBytes : 0, out, lse, stream);
+}
+
 mla_status mla_lse_combine(const float* part_o, const float* part_lse, int32_t num_parts,
                            int64_t rows, float* out, float* lse, void* stream) {
   if (num_parts < 1 || rows < 0) return MLA_ERR_INVALID_ARG;

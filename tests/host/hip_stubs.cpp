@@ -112,6 +112,13 @@ hipError_t launch_combine_project(const float*, const float*, int nparts, int T,
   return hipSuccess;
 }
 
+hipError_t noalloc_scratch(void** ptr) {
+  // A fake, never dereferenced device address (the stub decode launch only
+  // walks the plan).
+  *ptr = reinterpret_cast<void*>(uintptr_t(1) << 40);
+  return hipSuccess;
+}
+
 }  // namespace mla
 
 extern "C" hipError_t hipGetDevice(int* d) {
