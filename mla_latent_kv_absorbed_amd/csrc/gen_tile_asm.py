@@ -95,6 +95,7 @@ from __future__ import annotations
 
 import math
 import os
+import re
 
 SCRATCH_HI = 255   # rings are allocated downwards from here
 
@@ -492,7 +493,23 @@ def dq_program_mx(base: int):
 
 
 def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
-              tail_chains: int = 2, dq: bool = False, dqmx: bool = False):
+              tail_chains: int = 2, dq: bool = False, dqmx: bool = False,
+              one_chain: bool = False, lead_pv: int = 0, gate=None, subst=None,
+              gld_fmt=None, tail: bool = True, keep_m0: bool = False, addr=None,
+              early_prep: bool = False):
+    """One statement (see the module docstring).  The keyword arguments after
+    dqmx serve the FP8 unit loop (fp8_loop): one_chain puts every QK MFMA
+    on the chain %[s]; lead_pv schedules that many PV MFMAs before the first
+    QK MFMA; gate = (pos, lines) emits `lines` (the loop's barrier and DMA
+    set-up) before the MFMA at position pos and holds every K read back
+    until then; subst maps operand texts to literal registers; gld_fmt
+    formats the DMA rows in place of the MLA_GLD macro; tail False leaves
+    out the closing waits for the MFMA results; keep_m0 leaves M0 to the
+    caller; addr maps the LDS address operands (%[kb], %[va], %[vb], %[sc])
+    to (register, byte delta) so that a buffer's reads become constant
+    offsets from a base register; early_prep waits for the next MFMA's
+    operand read and widens or duplicates it in the middle of the current
+    slot, so that the MFMA needs no s_nop."""
     reads = {}
     kops, vops = [], []
     if qk:
@@ -555,7 +572,9 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
     # S chains: QK-only statements alternate two chains; with PV one chain
     # while PV MFMAs separate its steps, and two for the tail.
     for i, op in enumerate(kops):
-        if not pv:
+        if one_chain:
+            op.acc = "s"
+        elif not pv:
             op.acc = "s" if i % 2 == 0 else "s1"
         else:
             tail = i - len(vops)
@@ -563,7 +582,8 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
     # Spread the PV MFMAs evenly between the QK MFMAs (one for one when the
     # counts match), so the dependent S chain is broken up along the whole
     # statement.
-    ops = []
+    ops = list(vops[:lead_pv])
+    vops = vops[lead_pv:]
     j = 0
     for i, kop in enumerate(kops):
         ops.append(kop)
@@ -593,8 +613,9 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
         rings["DQ"] = (1, 9)
     st = Stream(rings)
     st.emit("s_nop 2")  # operands may have just been written by VALU instructions
-    if n_dma:
+    if n_dma and not keep_m0:
         st.emit("s_mov_b32 %[m0s], m0")  # M0 is handed back unchanged
+    gate_open = [gate is None]
 
     smp = sm_program(fp8, st.base["SK"], st.base["ST"]) if sm else []
     if dq:
@@ -612,6 +633,8 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
     state = {"pos": -1}  # last issued MFMA
 
     def slot_free(ring):
+        if ring == "KR" and not gate_open[0]:
+            return False
         q, k = queue[ring], nxt[ring]
         size = rings[ring][0]
         return k < len(q) and (k < size or q[k - size] in freed)
@@ -714,6 +737,11 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
     started = set()
     fill()
     for i, op in enumerate(ops):
+        if gate is not None and i == gate[0]:
+            for line in gate[1]:
+                st.emit(line)
+            gate_open[0] = True
+            fill()
         ensure(op.read)
         x = st.reg(reads[op.read].ring, slot_of[op.read]) + op.xoff
         gap = len(st.lines) - st.last_valu[x] if x in st.last_valu else 2
@@ -729,28 +757,278 @@ def statement(fp8: bool, qk: bool, pv: bool, sm: bool = False, n_dma: int = 0,
         if i >= 1:
             release_direct(ops[i - 1].read)
         for k in dma_at.get(i, []):
+            assert gate_open[0], "a DMA row before the gate"
             st.emit("s_mov_b32 m0, %[m0b]" if k == 0 else "s_add_u32 m0, m0, 3968")
             st.emit("s_nop 0")
-            st.emit(f"@GLD({128 * k})")
+            st.emit(gld_fmt.format(off=128 * k) if gld_fmt else f"@GLD({128 * k})")
         if i >= 1:
-            sm_emit(per_slot, i)
+            if early_prep and i + 1 < n:
+                nr = reads[ops[i + 1].read]
+                half = per_slot // 2
+                sm_emit(half, i)
+                if (nr.dup_half or nr.widen_inplace) and ops[i + 1].read in issued:
+                    ensure(ops[i + 1].read)
+                sm_emit(per_slot - half, i)
+            else:
+                sm_emit(per_slot, i)
         fill()
     sm_emit(len(smp))
     for rid in reads:
         assert rid in issued, f"read {rid} never issued"
     if sm:
         st.emit("s_waitcnt lgkmcnt(0)")
-    if n_dma:
+    if n_dma and not keep_m0:
         st.emit("s_mov_b32 m0, %[m0s]")
-    if ops:
-        # S chains are read by VALU code next; O accumulators may be read by
-        # v_accvgpr_read next: wait out the MFMA write latency.
-        st.emit("s_nop 7")
-        st.emit("s_nop 7")
-        st.emit("s_nop 7")
-    elif sm:
-        st.emit("s_nop 1")  # the last results are packed by VALU just above
-    return st.lines, st.lowest
+    if tail:
+        if ops:
+            # S chains are read by VALU code next; O accumulators may be read by
+            # v_accvgpr_read next: wait out the MFMA write latency.
+            st.emit("s_nop 7")
+            st.emit("s_nop 7")
+            st.emit("s_nop 7")
+        elif sm:
+            st.emit("s_nop 1")  # the last results are packed by VALU just above
+    lines = st.lines
+    if addr:
+        def reloc(m):
+            reg, delta = addr[m.group(1)]
+            off = int(m.group(2)) + delta
+            assert 0 <= off < 65536, off
+            return f"{reg} offset:{off}"
+        pat_a = re.compile(r"(%\[(?:kb|va|vb|sc)\]) offset:(\d+)")
+        lines = [pat_a.sub(reloc, l) for l in lines]
+    if subst:
+        keys = sorted(subst, key=len, reverse=True)
+        pat = re.compile("|".join(re.escape(k) for k in keys))
+        lines = [pat.sub(lambda m: subst[m.group(0)], l) for l in lines]
+    return lines, st.lowest
+
+
+# ---------------------------------------------------------------- FP8 unit loop
+
+# Literal registers of MLA_LOOP_FP8_ASM below the statement scratch rings
+# (v216..v255).
+LOOP_SA, LOOP_SB, LOOP_PB = 168, 184, 200    # score sets A, B; P of the next P.V
+LOOP_PSCP, LOOP_PSCC, LOOP_ALPHA = 208, 209, 210
+LOOP_KB = (160, 161, 162)   # tiles + K lane offset (+ 3, 6 tile buffers)
+LOOP_VB = (163, 164, 165)   # tiles + V^T lane offset (+ 3, 6 tile buffers)
+LOOP_SC0 = 166              # scale ring + the lane's scale offset
+LOOP_BPA = 167              # byte address of lane ^ 32
+LOOP_VOFF, LOOP_SOFF, LOOP_TOK, LOOP_CHOFF, LOOP_DYN = 211, 212, 213, 214, 215
+LOOP_VLOW = 160
+# s36 it, s37 jlast - (j0 + 32 (it + lead)), s38 table entry of tile it +
+# lead, s39 lim_min, s40 mask flag, s41..s44 temporaries, s45 row DMA M0,
+# s[46:47] pool row base, s[48:49] scale base, s[50:51] saved EXEC, s52 saved
+# M0, s53 ntiles - 1, s54 the rescale's return site, s55 table byte offset of
+# the next entry load, s56 its largest value, s57 tiles + 1024 w, s58 ns - 1,
+# s59 the row size 576.
+LOOP_SGPRS = (36, 59)
+FP8_RING = 8             # tile buffers (the unit loop is unrolled by the ring size)
+FP8_LEAD = FP8_RING - 2  # tiles the DMA runs ahead
+FP8_TILE_BYTES = 36 * 512
+LOOP_LEAD_PV = 3         # P.V MFMAs at the head of a step (one before the barrier)
+
+
+def fp8_loop():
+    """The whole tile loop of one FP8 unit (paged tables, a wave with rows, at
+    least two tiles) as one statement, from S^T of tile 0 to the last P.V.
+
+    Iteration it (tile it in ring buffer it % 8): the statement of the steady
+    state (S^T of tile it+1, the softmax of tile it, O^T += V^T . P^T of tile
+    it-1), with the DMA of tile it+lead issued after the workgroup barrier.
+    The loop is unrolled by the ring size, so every LDS operand address is a
+    constant offset from a base register set up once per unit.  The barrier
+    and the DMA set-up come after the first P.V MFMA (P.V needs no barrier:
+    V of tile it-1 and P are in place), so the wait overlaps a running MFMA;
+    the K reads of tile it+1 are held back until after it and land while the
+    next P.V MFMAs run.  The two score sets swap roles from one iteration to
+    the next, so that nothing is copied but the 8 registers of P.
+
+    Operands (besides the Q operands, the accumulators and the softmax
+    scalars of the other statements): %[tiles], %[scb] LDS bases of the tile
+    ring and of the scale ring; %[ke], %[vao], %[scl], %[bpa] the lane parts of
+    the K, V^T and scale addresses and the lane ^ 32 address; %[tok],
+    %[choff] the lane's DMA token and chunk offset; %[pool_lo/hi],
+    %[kvs_lo/hi], %[trow] the pool, the scales and this request's table row;
+    %[j0], %[jlast], %[ntiles], %[ns], %[w] the unit's first and last local
+    index, its tile count, the pool's slot count and the wave index;
+    %[raw0] the table entry of tile lead; %[limmin] the unit's lim_min;
+    %[mref], %[lsum], %[limh] (read-write) as in the softmax.
+    """
+    A, B, PB = LOOP_SA, LOOP_SB, LOOP_PB
+    R, lead, T = FP8_RING, FP8_LEAD, FP8_TILE_BYTES
+
+    def kaddr(buf):
+        return (f"v{LOOP_KB[buf // 3]}", (buf % 3) * T)
+
+    def vaddr(buf):
+        return (f"v{LOOP_VB[buf // 3]}", (buf % 3) * T)
+
+    def addr_static(buf):
+        # K of tile it+1, V^T of tile it-1, the scales of tile it.
+        kr, kd = kaddr((buf + 1) % R)
+        vr, vd = vaddr((buf - 1) % R)
+        return {"%[kb]": (kr, kd), "%[va]": (vr, vd), "%[vb]": (vr, vd + 256),
+                "%[sc]": (f"v{LOOP_SC0}", 128 * buf)}
+
+    def subst(cur, nxt):
+        d = {f"%[x{i}]": f"v{cur + i}" for i in range(16)}
+        d.update({"%[s]": f"v[{nxt}:{nxt + 15}]", "%[pp]": f"v[{PB}:{PB + 7}]",
+                  "%[pscv]": f"v{LOOP_PSCP}", "%[psco]": f"v{LOOP_PSCC}",
+                  "%[alpha]": f"v{LOOP_ALPHA}", "%[mon]": "s40", "%[m0b]": "s45",
+                  "%[bpa]": f"v{LOOP_BPA}"})
+        return d
+
+    gld = f"global_load_lds_dwordx4 v{LOOP_VOFF}, s[46:47] offset:{{off}}"
+
+    def mask_flag():
+        return ["s_cmp_lt_i32 s39, 31", "s_cselect_b32 s40, 1, 0"]
+
+    def gate(buf):
+        # After the barrier: DMA of tile it+lead (a clamped copy of the
+        # unit's last token past its end) into buffer it-2, whose last
+        # reader (P.V of tile it-2) every wave has passed.  s38, the table
+        # entry of tile it+lead, was loaded during the previous statement,
+        # whose final lgkmcnt(0) it has passed; the entry of tile it+1+lead
+        # is loaded here and waited for by this statement's final lgkmcnt(0).
+        bd = (buf - 2) % R
+        return [
+            f"s_waitcnt vmcnt({5 * (lead - 2)})",             # own share of tile it+1
+            "s_barrier",
+            "s_max_i32 s41, s38, 0",
+            "s_min_i32 s41, s41, s58",                       # raw_c
+            "s_load_dword s38, %[trow], s55",                # entry of tile it+1+lead
+            "s_add_u32 s55, s55, 0x80",
+            "s_min_u32 s55, s55, s56",
+            "s_sub_i32 s42, s58, s41",                       # ns - 1 - raw_c
+            "s_max_i32 s43, s37, 0",
+            "s_min_i32 s43, s43, s42",
+            "s_min_i32 s43, s43, 31",                        # lim of the tile
+            f"v_min_i32 v{LOOP_VOFF}, s43, v{LOOP_TOK}",      # token of this lane
+            f"v_lshlrev_b32 v{LOOP_SOFF}, 2, v{LOOP_VOFF}",
+            f"v_mad_u32_u24 v{LOOP_VOFF}, v{LOOP_VOFF}, s59, v{LOOP_CHOFF}",
+            "s_mul_i32 s46, s41, 0x240",
+            "s_mul_hi_u32 s47, s41, 0x240",
+            "s_add_u32 s46, s46, %[pool_lo]",
+            "s_addc_u32 s47, s47, %[pool_hi]",               # pool row of raw_c
+            "s_lshl_b32 s48, s41, 2",
+            "s_lshr_b32 s49, s41, 30",
+            "s_add_u32 s48, s48, %[kvs_lo]",
+            "s_addc_u32 s49, s49, %[kvs_hi]",                # its scale
+            f"s_add_u32 s45, s57, {bd * T}",                 # M0 of the row DMA
+            # waves 0, 1: row instruction 4; waves 2, 3 (lanes 0..31): the scales
+            "s_cmp_lt_u32 %[w], 2",
+            "s_cbranch_scc0 61f",
+            "s_add_u32 m0, s45, 0x3e00",
+            "s_nop 0",
+            f"global_load_lds_dwordx4 v{LOOP_VOFF}, s[46:47] offset:512",
+            "s_branch 62f",
+            "61:",
+            f"s_add_u32 m0, %[scb], {128 * bd}",
+            "s_mov_b64 s[50:51], exec",
+            "s_mov_b32 exec_hi, 0",
+            "s_nop 0",
+            f"global_load_lds_dword v{LOOP_SOFF}, s[48:49] offset:0",
+            "s_mov_b64 exec, s[50:51]",
+            "62:",
+        ]
+
+    # O *= alpha when some row's running max moved: one out-of-line block
+    # (label 80) shared by every site; s54 says where to return.
+    sites = []
+
+    def rescale():
+        k = len(sites)
+        sites.append(70 + k)
+        return [f"v_cmp_neq_f32 vcc, 1.0, v{LOOP_ALPHA}", f"s_mov_b32 s54, {k}",
+                "s_cbranch_vccnz 80f", f"{70 + k}:"]
+
+    def take_p(cur):
+        return [f"v_mov_b64 v[{PB + 2 * k}:{PB + 2 * k + 1}], v[{cur + 2 * k}:{cur + 2 * k + 1}]"
+                for k in range(4)] + [f"v_mov_b32 v{LOOP_PSCP}, v{LOOP_PSCC}"]
+
+    def advance():
+        # it += 1; the mask limits and the DMA's tile limit move by one tile.
+        return ["s_add_u32 s36, s36, 1", "v_add_u32 %[limh], -32, %[limh]",
+                "s_add_i32 s39, s39, -32", "s_add_i32 s37, s37, -32"]
+
+    def step(cur, nxt, buf, first):
+        body, _ = statement(fp8=True, qk=True, pv=not first, sm=True, n_dma=4, tail_chains=1,
+                            one_chain=True, lead_pv=0 if first else LOOP_LEAD_PV,
+                            gate=(0 if first else 1, gate(buf)), subst=subst(cur, nxt),
+                            gld_fmt=gld, keep_m0=True, tail=False, addr=addr_static(buf),
+                            early_prep=True)
+        return body
+
+    def exit_to(nxt, buf_next):
+        # The next tile (it, in buffer buf_next, scores in set nxt) is the last.
+        return [f"s_mov_b32 s44, {buf_next}", "s_cmp_eq_u32 s36, s53",
+                f"s_cbranch_scc1 {65 if nxt == A else 66}f"]
+
+    out = ["s_mov_b32 s52, m0", "s_mov_b32 s36, 0", "s_mov_b32 s38, %[raw0]",
+           "s_mov_b32 s39, %[limmin]", "s_add_i32 s53, %[ntiles], -1",
+           "s_sub_i32 s37, %[jlast], %[j0]", f"s_add_i32 s37, s37, {-32 * lead}",
+           "s_lshl_b32 s56, s53, 5", "s_add_u32 s56, s56, %[j0]", "s_lshl_b32 s56, s56, 2",
+           f"s_add_u32 s55, %[j0], {32 * (lead + 1)}", "s_lshl_b32 s55, s55, 2",
+           "s_min_u32 s55, s55, s56",
+           "s_lshl_b32 s57, %[w], 10", "s_add_u32 s57, s57, %[tiles]",
+           "s_add_i32 s58, %[ns], -1", "s_movk_i32 s59, 0x240",
+           f"v_add_u32 v{LOOP_KB[0]}, %[tiles], %[ke]",
+           f"v_add_u32 v{LOOP_KB[1]}, {3 * T}, v{LOOP_KB[0]}",
+           f"v_add_u32 v{LOOP_KB[2]}, {6 * T}, v{LOOP_KB[0]}",
+           f"v_add_u32 v{LOOP_VB[0]}, %[tiles], %[vao]",
+           f"v_add_u32 v{LOOP_VB[1]}, {3 * T}, v{LOOP_VB[0]}",
+           f"v_add_u32 v{LOOP_VB[2]}, {6 * T}, v{LOOP_VB[0]}",
+           f"v_add_u32 v{LOOP_SC0}, %[scb], %[scl]",
+           f"v_mov_b32 v{LOOP_BPA}, %[bpa]", f"v_mov_b32 v{LOOP_TOK}, %[tok]",
+           f"v_mov_b32 v{LOOP_CHOFF}, %[choff]"]
+    # S^T of tile 0 (buffer 0) into A (two chains, A and B, summed).
+    qk0, _ = statement(fp8=True, qk=True, pv=False,
+                       subst={"%[s]": f"v[{A}:{A + 15}]", "%[s1]": f"v[{B}:{B + 15}]"},
+                       addr={"%[kb]": kaddr(0)})
+    out += qk0
+    out += [f"v_add_f32 v{A + i}, v{A + i}, v{B + i}" for i in range(16)]
+    # it = 0: S^T of tile 1 into B, softmax of tile 0 (no P.V yet).
+    out += mask_flag() + step(A, B, 0, True) + take_p(A) + advance() + exit_to(B, 1)
+    # Steady state, unrolled by the ring size: iteration it sits at position
+    # it % 8, its buffer; odd it: softmax on B, S^T into A.
+    out += ["63:"]
+    for k in range(R):
+        buf = (1 + k) % R
+        cur, nxt = (B, A) if buf % 2 else (A, B)
+        out += mask_flag() + step(cur, nxt, buf, False) + rescale() + take_p(cur) + advance()
+        if k < R - 1:
+            out += exit_to(nxt, (buf + 1) % R)
+        else:
+            out += [f"s_mov_b32 s44, {(buf + 1) % R}", "s_cmp_eq_u32 s36, s53",
+                    f"s_cbranch_scc0 63b", f"s_branch {65 if nxt == A else 66}f"]
+
+    def last(cur):
+        # The last tile, in buffer s44 (scores in set cur): its softmax with
+        # P.V of the tile before, then its own P.V; addresses from s44.
+        dyn = {"%[va]": (f"v{LOOP_DYN}", 0), "%[vb]": (f"v{LOOP_DYN}", 256),
+               "%[sc]": (f"v{LOOP_TOK}", 0)}
+        smpv, _ = statement(fp8=True, qk=False, pv=True, sm=True, subst=subst(cur, cur),
+                            addr=dyn)
+        pv, _ = statement(fp8=True, qk=False, pv=True, subst=subst(cur, cur), addr=dyn)
+        pre = ["s_add_u32 s41, s44, 7", "s_and_b32 s41, s41, 7",
+               f"s_mul_i32 s41, s41, {T}",
+               f"v_add_u32 v{LOOP_DYN}, s41, v{LOOP_VB[0]}",      # V^T of tile it-1
+               "s_lshl_b32 s42, s44, 7",
+               f"v_add_u32 v{LOOP_TOK}, s42, v{LOOP_SC0}"]       # scales of tile it
+        own = [f"s_mul_i32 s41, s44, {T}",
+               f"v_add_u32 v{LOOP_DYN}, s41, v{LOOP_VB[0]}"]     # V^T of tile it
+        return pre + mask_flag() + smpv + rescale() + take_p(cur) + own + pv
+
+    out += ["65:"] + last(A) + ["s_branch 67f"]
+    out += ["66:"] + last(B)
+    out += ["67:", "s_mov_b32 m0, s52", "s_branch 69f"]
+    lines, _ = rescale_statement()
+    out += ["80:"] + [l.replace("%[al]", f"v{LOOP_ALPHA}") for l in lines]
+    for k, lab in enumerate(sites):
+        out += [f"s_cmp_eq_u32 s54, {k}", f"s_cbranch_scc1 {lab}b"]
+    out += ["69:"]
+    return out
 
 
 def rescale_statement():
@@ -815,6 +1093,11 @@ def generate() -> str:
         out.append(emit_macro(name, lines))
         regs = ", ".join(f'"v{r}"' for r in range(low, SCRATCH_HI + 1))
         out.append(f"// Scratch registers of {name}.\n#define {name[:-4]}_CLOBBERS {regs}, \"memory\"\n")
+    out.append(emit_macro("MLA_LOOP_FP8_ASM", fp8_loop()))
+    regs = ", ".join(f'"v{r}"' for r in range(LOOP_VLOW, SCRATCH_HI + 1))
+    sregs = ", ".join(f'"s{r}"' for r in range(LOOP_SGPRS[0], LOOP_SGPRS[1] + 1))
+    out.append("// Scratch registers of MLA_LOOP_FP8_ASM.\n#define MLA_LOOP_FP8_CLOBBERS "
+               f"{regs}, {sregs}, \"vcc\", \"scc\", \"memory\"\n")
     return "\n".join(out)
 
 

@@ -113,12 +113,22 @@ def test_statements_found():
     assert "MLA_STEP_FP8_ASM" in STATEMENTS and "MLA_FUSED_BF16_ASM" in STATEMENTS
 
 
+def _literal_sgprs(text):
+    regs = set()
+    for m in re.finditer(r"(?<![%\w])s\[(\d+):(\d+)\]", text):
+        regs.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    for m in re.finditer(r"(?<![%\w\[])s(\d+)(?![\d:])", text):
+        regs.add(int(m.group(1)))
+    return regs
+
+
 @pytest.mark.parametrize("name", STATEMENTS)
 def test_literal_registers_are_clobbered(name):
-    text = "".join(_instrs(name))
+    text = " ".join(_instrs(name))
     declared = set(int(x) for x in re.findall(r'"v(\d+)"', _clobbers(name)))
     assert _literal_vgprs(text) <= declared
-    assert not re.search(r"(?<![%\w\[])s(\d+)\b", text), "literal SGPRs are not allowed"
+    declared_s = set(int(x) for x in re.findall(r'"s(\d+)"', _clobbers(name)))
+    assert _literal_sgprs(text) <= declared_s, "a literal SGPR that is not declared clobbered"
 
 
 @pytest.mark.parametrize("name", STATEMENTS)
@@ -145,10 +155,15 @@ def test_m0_restored(name):
     if not writes:
         assert not any(i.startswith("global_load_lds") for i in ins)
         return
-    # Saved before M0 is first touched, restored by the last write, and no
-    # DMA (which reads M0) after the restore.
-    assert ins[touch[0]] == "s_mov_b32 %[m0s], m0"
-    assert ins[writes[-1]] == "s_mov_b32 m0, %[m0s]"
+    # Saved before M0 is first touched (in %[m0s], or in a literal SGPR the
+    # statement declares clobbered), restored from it by the last write, and
+    # no DMA (which reads M0) after the restore.
+    m = re.fullmatch(r"s_mov_b32 (%\[m0s\]|s\d+), m0", ins[touch[0]])
+    assert m, ins[touch[0]]
+    save = m.group(1)
+    if save.startswith("s"):
+        assert f'"{save}"' in _clobbers(name)
+    assert ins[writes[-1]] == f"s_mov_b32 m0, {save}"
     assert not any(i.startswith("global_load_lds") for i in ins[writes[-1]:])
 
 
@@ -170,10 +185,12 @@ def test_call_sites_declare_outputs_and_flags(name):
         assert not missing, f"operands written but not declared as outputs: {sorted(missing)}"
         if _clobbers(name):
             assert name[: -len("_ASM")] + "_CLOBBERS" in clob
+        # SCC / VCC declared at the call site or in the statement's clobber macro.
+        flags = clob + _clobbers(name)
         if writes_scc:
-            assert '"scc"' in clob
+            assert '"scc"' in flags
         if writes_vcc:
-            assert '"vcc"' in clob
+            assert '"vcc"' in flags
         # Outputs written before the last input is read must be early-clobber
         # (or tied read-write) so that no input shares their register.
         for op, cons in re.findall(r"\[(\w+)\]\s*\"([=+][^\"]*)\"", outputs):
