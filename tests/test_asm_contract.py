@@ -267,3 +267,41 @@ def test_block_depths_parsed():
             "\ts_endpgm"]
     got = [(b["lines"][0].split(":")[0], b["depth"]) for b in _blocks_with_depth(body)]
     assert got == [(".LBB0_1", 0), (".LBB0_2", 2), ("; %bb.3", 2), (".LBB0_4", 0)]
+
+
+# ------------------------------------------------------------ launch shapes
+
+def _hip_sources():
+    return {f: open(os.path.join(CSRC, f)).read()
+            for f in sorted(os.listdir(CSRC)) if f.endswith(".hip")}
+
+
+def test_every_kernel_is_launched_within_its_launch_bounds():
+    """Every __global__ kernel declares __launch_bounds__, and every launch
+    of it uses a block no larger than that bound: the register budget the
+    compiler gives a kernel (the decode kernel: 512 registers, one wave per
+    SIMD) only holds for the block size it was told."""
+    bounds = {}
+    for f, text in _hip_sources().items():
+        for m in re.finditer(r"__global__\s+(__launch_bounds__\((\d+)(?:,\s*\d+)?\)\s+)?void\s+(\w+)",
+                             text):
+            assert m.group(1), f"{f}: kernel {m.group(3)} has no __launch_bounds__"
+            bounds[m.group(3)] = int(m.group(2))
+    assert {"decode_kernel", "merge_split_kernel", "merge_split_wave_kernel",
+            "lse_combine_kernel", "prepare_kernel", "combine_project_kernel"} <= set(bounds)
+    launches = 0
+    for f, text in _hip_sources().items():
+        for m in re.finditer(r"hipLaunchKernelGGL\(\s*(\w+)\s*,[^,]*,\s*dim3\((\d+)\)", text):
+            kernel, block = m.group(1), int(m.group(2))
+            # decode_kernel is launched through a pointer to one of its
+            # instantiations (`kernel`).
+            name = "decode_kernel" if kernel == "kernel" else kernel
+            assert name in bounds, f"{f}: launch of unknown kernel {kernel}"
+            assert block <= bounds[name], f"{f}: {kernel} launched with {block} > {bounds[name]}"
+            launches += 1
+    assert launches >= 7
+    # ... and `go`, the lambda that launches `kernel`, is only ever handed
+    # instantiations of decode_kernel.
+    text = _hip_sources()["mla_kernels.hip"]
+    handed = re.findall(r"\bgo\((\w+)<", text)
+    assert handed and set(handed) == {"decode_kernel"}, handed
