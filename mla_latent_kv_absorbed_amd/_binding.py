@@ -93,11 +93,11 @@ def status_string(status: int) -> str:
 
 
 # Plan header fields, in the order of mla::PlanHeader (csrc/plan_layout.h).
-_HEADER = struct.Struct("<2I18i3q")
+_HEADER = struct.Struct("<2I18i4q")
 _HEADER_NAMES = ("magic", "version", "batch", "q_len", "num_heads", "rows", "row_groups",
                  "num_wgs", "num_units", "num_parts", "num_split_reqs", "kv_dtype", "dcp_size",
                  "dcp_rank", "off_wg", "off_units", "off_reqs", "off_split", "max_local",
-                 "page_size", "plan_bytes", "workspace_bytes", "ws_lse_offset")
+                 "page_size", "plan_bytes", "workspace_bytes", "ws_lse_offset", "ws_sc_offset")
 
 
 def _aligned_bytes(n: int) -> np.ndarray:

@@ -23,16 +23,17 @@ struct DecodeArgs {
   float c2;                  // softmax_scale * log2(e)
   float* out;                // [B, M, 512]
   float* lse;                // [B, M]
-  float* ws_o;               // [parts, M, 512]
+  uint16_t* ws_o;            // [parts, M, 512] fp16 bits of O_part / ws_sc (split partials)
   float* ws_lse;             // [parts, M]
+  float* ws_sc;              // [parts, M] power-of-two factor of each partial row
 };
 
 hipError_t launch_decode(int kv, bool paged, int grid, const DecodeArgs& args,
                          hipStream_t stream);
 // max_parts: the largest part count of any split request in the plan.
 hipError_t launch_merge_split(const uint8_t* plan_dev, int num_split_reqs, int rows,
-                              int max_parts, const float* ws_o, const float* ws_lse, float* out,
-                              float* lse, hipStream_t stream);
+                              int max_parts, const uint16_t* ws_o, const float* ws_lse,
+                              const float* ws_sc, float* out, float* lse, hipStream_t stream);
 // Device address of the current device's no-alloc scratch array (capacity
 // kNoAllocScratchBytes), looked up once per device with hipGetSymbolAddress.
 constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;

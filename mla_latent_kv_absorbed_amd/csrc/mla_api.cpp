@@ -374,9 +374,13 @@ mla_status mla_decode_plan(const mla_decode_desc* d, const int32_t* seq_lens_hos
   h->max_local = (int32_t)max_local;
   h->page_size = d->page_size;
   h->plan_bytes = lay.total;
-  const int64_t ws_o_bytes = (int64_t)total_parts * M * kLatent * 4;
+  // Split partials: O in fp16, each row scaled by a power of two (its factor
+  // in the ws_sc array), then the partial LSE and the factors in fp32.
+  const int64_t ws_o_bytes = (int64_t)total_parts * M * kLatent * 2;
+  const int64_t ws_row_bytes = (int64_t)total_parts * M * 4;
   h->ws_lse_offset = align_up(ws_o_bytes, 256);
-  h->workspace_bytes = total_parts > 0 ? align_up(h->ws_lse_offset + (int64_t)total_parts * M * 4, 256) : 0;
+  h->ws_sc_offset = align_up(h->ws_lse_offset + ws_row_bytes, 256);
+  h->workspace_bytes = total_parts > 0 ? align_up(h->ws_sc_offset + ws_row_bytes, 256) : 0;
 
   int32_t* wgb = reinterpret_cast<int32_t*>(base + lay.off_wg);
   Unit* units = reinterpret_cast<Unit*>(base + lay.off_units);
@@ -464,10 +468,10 @@ mla_status decode_args(const void* plan_host, const void* plan_device, const voi
   a->c2 = softmax_scale * 1.4426950408889634f;
   a->out = out;
   a->lse = lse;
-  a->ws_o = static_cast<float*>(workspace);
-  a->ws_lse = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                                   h->ws_lse_offset)
-                        : nullptr;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a->ws_o = reinterpret_cast<uint16_t*>(ws);
+  a->ws_lse = ws ? reinterpret_cast<float*>(ws + h->ws_lse_offset) : nullptr;
+  a->ws_sc = ws ? reinterpret_cast<float*>(ws + h->ws_sc_offset) : nullptr;
   *header = h;
   return MLA_OK;
 }
@@ -505,9 +509,10 @@ mla_status mla_decode_merge(const void* plan_host, const void* plan_device, cons
   if ((int64_t)workspace_bytes < h->workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (h->num_split_reqs == 0) return MLA_OK;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MLA_ERR_INVALID_ARG;
-  const float* ws_o = static_cast<const float*>(workspace);
-  const float* ws_lse = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) +
-                                                       h->ws_lse_offset);
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  const uint16_t* ws_o = reinterpret_cast<const uint16_t*>(ws);
+  const float* ws_lse = reinterpret_cast<const float*>(ws + h->ws_lse_offset);
+  const float* ws_sc = reinterpret_cast<const float*>(ws + h->ws_sc_offset);
   const uint8_t* blob = static_cast<const uint8_t*>(plan_host);
   const ReqParts* reqs = reinterpret_cast<const ReqParts*>(blob + h->off_reqs);
   const int32_t* split = reinterpret_cast<const int32_t*>(blob + h->off_split);
@@ -515,7 +520,7 @@ mla_status mla_decode_merge(const void* plan_host, const void* plan_device, cons
   for (int i = 0; i < h->num_split_reqs; ++i)
     max_parts = reqs[split[i]].num_parts > max_parts ? reqs[split[i]].num_parts : max_parts;
   if (launch_merge_split(static_cast<const uint8_t*>(plan_device), h->num_split_reqs, h->rows,
-                         max_parts, ws_o, ws_lse, out, lse,
+                         max_parts, ws_o, ws_lse, ws_sc, out, lse,
                          static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;

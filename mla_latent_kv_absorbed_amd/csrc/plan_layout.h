@@ -7,7 +7,7 @@
 namespace mla {
 
 constexpr uint32_t kPlanMagic = 0x504C414Du;  // "MALP"
-constexpr uint32_t kPlanVersion = 1;
+constexpr uint32_t kPlanVersion = 2;
 
 constexpr int kLatent = 512;    // kv_lora_rank: width of c_kv and of the output
 constexpr int kRope = 64;       // qk_rope_head_dim
@@ -42,8 +42,9 @@ struct PlanHeader {
   int64_t plan_bytes;
   int64_t workspace_bytes;
   int64_t ws_lse_offset;  // byte offset of the partial LSE array in the workspace
+  int64_t ws_sc_offset;   // byte offset of the partial rows' power-of-two factors
 };
-static_assert(sizeof(PlanHeader) == 104, "plan header layout");
+static_assert(sizeof(PlanHeader) == 112, "plan header layout");
 
 // One work unit: row group g of request b over local token range [j0, j1).
 // part < 0: the unit covers the request's whole range, write the output;

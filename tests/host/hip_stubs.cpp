@@ -86,7 +86,8 @@ hipError_t launch_decode(int kv, bool paged, int grid, const DecodeArgs& a, hipS
 }
 
 hipError_t launch_merge_split(const uint8_t*, int num_split_reqs, int rows, int max_parts,
-                              const float*, const float*, float*, float*, hipStream_t) {
+                              const uint16_t*, const float*, const float*, float*, float*,
+                              hipStream_t) {
   ++g_merge_launches;
   REQUIRE(num_split_reqs > 0 && rows > 0 && max_parts > 1);
   return hipSuccess;

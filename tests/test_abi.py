@@ -163,10 +163,20 @@ def test_decode_and_combine_reject_bad_arguments_on_host():
 def test_plan_header_fields():
     p = mla.make_plan(_desc(batch=3, dcp_size=8, dcp_rank=5), [100000, 8, 6])
     h = p.header
-    assert h["magic"] == 0x504C414D and h["version"] == 1
+    assert h["magic"] == 0x504C414D and h["version"] == 2
     assert h["rows"] == 480 and h["row_groups"] == 4
     assert h["max_local"] == 12500 and h["dcp_size"] == 8 and h["dcp_rank"] == 5
     assert h["plan_bytes"] == len(p.host) and h["page_size"] == 64
+    # Workspace of the split partials: O in fp16 [parts, M, 512], then the
+    # LSE and the row factors in fp32 [parts, M], each 256-byte aligned.
+    parts, M = h["num_parts"], h["rows"]
+    assert parts > 0
+
+    def up(x):
+        return -(-x // 256) * 256
+    assert h["ws_lse_offset"] == up(parts * M * 512 * 2)
+    assert h["ws_sc_offset"] == up(h["ws_lse_offset"] + parts * M * 4)
+    assert h["workspace_bytes"] == up(h["ws_sc_offset"] + parts * M * 4) == p.workspace_bytes
 
 
 def test_prepare_rejects_bad_arguments_on_host():

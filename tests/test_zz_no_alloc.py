@@ -62,7 +62,7 @@ def test_noalloc_matches_decode_on_two_calls(kv):
 
 
 def test_noalloc_rejects_plans_beyond_the_scratch():
-    # 64 requests x 8 splits x 1024 rows of fp32 partials: beyond 128 MiB.
+    # 64 requests x 8 splits x 1024 rows of fp16 partials (512 MiB): beyond 128 MiB.
     lens = [4096] * 64
     desc = mla.make_desc(64, 8, 128, "bf16", page_size=64, force_splits=8)
     plan = mla.make_plan(desc, lens, device=DEV)
