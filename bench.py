@@ -76,14 +76,32 @@ WORKLOADS = {
 }
 
 
-def kernel_source_hash() -> str:
-    """sha256 of the decode kernel's sources (to tell stale counter summaries)."""
+KERNEL_SOURCES = ("mla_kernels.hip", "tile_asm.inc", "kernels.h", "plan_layout.h", "mla_api.cpp")
+
+
+def source_code_hash(texts) -> str:
+    """sha256 of source texts with their comments and blank lines left out."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for fn in ("mla_kernels.hip", "tile_asm.inc", "kernels.h"):
-        with open(os.path.join(ROOT, "mla_latent_kv_absorbed_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
+    for text in texts:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
+        h.update(b"\0")
     return h.hexdigest()
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the decode kernel's code, to tell stale counter summaries:
+    the kernel, its generated statements, its headers and the planner that
+    cuts its work, without comments, so that rewording a comment does not
+    orphan a summary taken on the same code."""
+    texts = []
+    for fn in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mla_latent_kv_absorbed_amd", "csrc", fn)) as f:
+            texts.append(f.read())
+    return source_code_hash(texts)
 
 
 def committed_traffic(workload: str):
