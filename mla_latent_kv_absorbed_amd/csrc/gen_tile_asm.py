@@ -236,17 +236,27 @@ def sm_program(fp8: bool, sk: int, tmp: int):
     # Lazy rescale: the running max moves only when the tile max exceeds it
     # by more than 8 in the exponent, (m_t - mref) c2 > 8 (a row with no
     # visible token yet has mref = -inf and moves as soon as m_t is finite).
+    # One block: when no lane's max moves (the usual case) the new max is the
+    # old one and alpha = 1, and the branch skips the update; the two moves
+    # also keep the VALU-written VCC three instructions from its first use
+    # as a lane mask, and the move after the exponential keeps its result
+    # one instruction from its reader.
     valu(f"v_sub_f32 {t[1]}, {t[0]}, %[mref]", [t[0], "%[mref]"], [t[1]])
     valu(f"v_mul_f32 {t[1]}, %[c2], {t[1]}", [t[1]], [t[1]])
     valu(f"v_cmp_lt_f32 vcc, 8.0, {t[1]}", [t[1]], ["vcc"])
-    valu("s_nop 1", [], [])  # VALU-written VCC read as a lane mask
-    valu(f"v_cndmask_b32 {t[2]}, %[mref], {t[0]}, vcc", [t[0], "%[mref]", "vcc"], [t[2]])
-    valu(f"v_sub_f32 {t[3]}, %[mref], {t[2]}", ["%[mref]", t[2]], [t[3]])
-    valu(f"v_mul_f32 {t[3]}, %[c2], {t[3]}", [t[3]], [t[3]])
-    valu(f"v_exp_f32 {t[3]}, {t[3]}", [t[3]], [t[3]], kind="trans")
-    valu(f"v_mov_b32 %[mref], {t[2]}", [t[2]], ["%[mref]"])
-    valu(f"v_cndmask_b32 %[alpha], 1.0, {t[3]}, vcc", [t[3], "vcc"], ["%[alpha]"])
-    valu(f"v_mul_f32 %[lsum], %[lsum], %[alpha]", ["%[lsum]", "%[alpha]"], ["%[lsum]"])
+    lazy = [f"v_mov_b32 {t[2]}, %[mref]",
+            "v_mov_b32 %[alpha], 1.0",
+            "s_cbranch_vccz 89f",
+            f"v_cndmask_b32 {t[2]}, %[mref], {t[0]}, vcc",
+            f"v_sub_f32 {t[3]}, %[mref], {t[2]}",
+            f"v_mul_f32 {t[3]}, %[c2], {t[3]}",
+            f"v_exp_f32 {t[3]}, {t[3]}",
+            f"v_mov_b32 %[mref], {t[2]}",
+            f"v_cndmask_b32 %[alpha], 1.0, {t[3]}, vcc",
+            "v_mul_f32 %[lsum], %[lsum], %[alpha]",
+            "89:"]
+    prog.append(("block", lazy, [t[0], "%[mref]", "%[lsum]", "vcc"],
+                 [t[2], t[3], "%[alpha]", "%[mref]", "%[lsum]"], None))
     # m c2, floored so that an all-masked row (m = -inf) gives e = 0.
     valu(f"v_mul_f32 {t[3]}, %[c2], {t[2]}", [t[2]], [t[3]])
     valu(f"v_max_f32 {t[3]}, %[nfm], {t[3]}", [t[3]], [t[3]])
