@@ -263,11 +263,18 @@ def test_mtp_q1_companion_sampled():
 
 
 def test_dcp_shard_workload_sampled():
+    """A dcp8 shard (128 x 12500 local tokens, q5, h96, FP8) in the plan
+    bench.py times (every request in one piece: 512 units fill the chip):
+    three requests against the oracle, and all 128 against a run of the same
+    inputs with every request cut in three pieces and merged."""
     x = config_inputs(4, device=DEV, dcp_rank=3)
     out, lse = gpu_decode(x)
     reqs = [0, 77, 127]
     o_ref, l_ref = oracle(x, reqs=reqs)
     check(out[reqs], lse[reqs], o_ref, l_ref, tag="dcp8 shard 3, 128x12500 (requests 0, 77, 127)")
+    o3, l3 = gpu_decode(x, force_splits=3)
+    check(o3, l3, out.double().cpu().numpy(), lse.double().cpu().numpy(),
+          tag="dcp8 shard 3: three pieces merged vs one piece, all 128 requests")
 
 
 def test_dcp8_all_shards_and_combine_sampled():
@@ -315,12 +322,16 @@ def test_sweep_batches_200k_sampled(B):
 
 def test_sweep_batch24_200k_sampled():
     """The largest fixed sweep batch (24 x 200k, q5, h96, FP8) at full size, in
-    the plan the sweep times; the last request is checked against the oracle."""
+    the plan the sweep times: the last request against the oracle, and all 24
+    against a run of the same inputs with every request in one piece."""
     x = config_inputs(5, device=DEV, batch=24)
     out, lse = gpu_decode(x)
     reqs = [23]
     o_ref, l_ref = oracle(x, reqs=reqs)
     check(out[reqs], lse[reqs], o_ref, l_ref, tag="sweep 24x200k q5 h96 fp8 (request 23)")
+    o1, l1 = gpu_decode(x, force_splits=1)
+    check(out, lse, o1.double().cpu().numpy(), l1.double().cpu().numpy(),
+          tag="sweep 24x200k: planner cuts vs unsplit, all 24 requests")
 
 
 def test_sweep_ragged64_sampled():
