@@ -1,4 +1,4 @@
-"""Why the FP8 path feeds P to the P.V MFMA as two e4m3 terms (CPU only).
+"""Why the FP8 path feeds Q and P to their MFMAs as two e4m3 terms (CPU only).
 
 The FP8 decode kernel quantises P' = P * scale_t (the probability times the
 token's value scale) to e4m3 per row and 32-token tile, against a power-of-two
@@ -12,7 +12,13 @@ compare the resulting O with the oracle's, against the stated tolerances
 (max |dO| <= 2e-2, ||dO||_F / ||O||_F <= 1e-2).  Two terms stay far inside
 them.  One term, which would halve the P.V MFMA work, breaks the relative
 bound on the near-uniform distribution and the absolute bound on the planted
-one, so the kernel keeps two.  Nothing here runs the HIP path.
+one, so the kernel keeps two.
+
+The c_kv part of each query row goes to the Q.K MFMA the same way: the row
+is scaled by 2^(8-E), where 2^E bounds its largest |q_nope|, and split into
+hi = rne(q') and lo = rne(q' - hi).  Two terms give back the BF16 query
+almost exactly; one term (which would halve the c_kv part of Q.K) moves the
+planted rows' LSE past its 1e-3 bound.  Nothing here runs the HIP path.
 """
 
 import numpy as np
@@ -21,7 +27,7 @@ import pytest
 from oracle import mla_ref
 from workload import make_inputs
 
-TOL_O_MAX, TOL_O_REL = 2e-2, 1e-2
+TOL_O_MAX, TOL_O_REL, TOL_LSE = 2e-2, 1e-2, 1e-3
 
 
 def _rne_e4m3(x):
@@ -91,3 +97,67 @@ def test_two_e4m3_terms_of_p_hold_the_tolerance_and_one_does_not(variant):
         assert rel1 > TOL_O_REL, rel1
     else:
         assert max1 > TOL_O_MAX, max1
+
+
+def _signed_e4m3(x):
+    return np.sign(x) * _rne_e4m3(np.abs(x))
+
+
+def _quantised_query(q_nope, terms):
+    """Rows [H, 512] of q_nope as the FP8 path's e4m3 terms, back in float64:
+    q' = q 2^(8-E) with 2^E > max |q| of the row (E clamped to -118..135),
+    hi = rne(q'), lo = rne(q' - hi); the value is (hi + lo) 2^(E-8), or
+    hi 2^(E-8) with one term."""
+    e = np.frexp(np.abs(q_nope).max(axis=1, keepdims=True))[1].astype(np.float64)
+    s = np.exp2(8.0 - np.clip(e, -118.0, 135.0))
+    hi = _signed_e4m3(q_nope * s)
+    lo = _signed_e4m3(q_nope * s - hi)
+    return ((hi + lo) if terms == 2 else hi) / s
+
+
+def _outputs_with_quantised_q(x, terms):
+    """(O, LSE) of every (b, i) row with q_nope replaced by its e4m3 terms and
+    everything else exact, next to the oracle's (O, LSE)."""
+    nb = x.numpy_bits()
+    o_ref, l_ref = mla_ref.mla_decode_ref(nb["q_nope"], nb["q_rope"], nb["pool"], nb["kv_scale"],
+                                          nb["req_to_token"], nb["seq_lens"], x.q_len,
+                                          x.softmax_scale, x.kv_dtype)
+    o, l = np.zeros_like(o_ref), np.zeros_like(l_ref)
+    for b in range(x.batch):
+        for i in range(x.q_len):
+            pos = mla_ref.visible_positions(int(nb["seq_lens"][b]), x.q_len, i)
+            slots = mla_ref.gather_slots(nb["req_to_token"], b, mla_ref.local_index(pos, 1, 0))
+            keys = mla_ref.dequant_rows(nb["pool"], nb["kv_scale"], slots, "fp8")
+            q = mla_ref.query_rows(nb["q_nope"], nb["q_rope"], b, i)
+            q[:, :512] = _quantised_query(q[:, :512], terms)
+            o[b, i], l[b, i], _ = mla_ref.softmax_reduce(
+                mla_ref.scores(q, keys, x.softmax_scale), keys[:, :512])
+    return o, l, o_ref, l_ref
+
+
+def test_two_e4m3_terms_give_back_a_bf16_query():
+    # BF16 values (8 significant bits) over eight binades below the row
+    # maximum: hi + lo holds all of them (two 4-bit terms; the smallest
+    # residual, 2^-7 of its element's binade, stays above the e4m3 subnormal
+    # step after the scaling by 2^(8-E)).
+    rng = np.random.default_rng(3)
+    m = rng.integers(0, 128, (8, 512))
+    k = rng.integers(-8, 0, (8, 512))
+    q = rng.choice([-1.0, 1.0], (8, 512)) * (1.0 + m / 128.0) * np.exp2(k)
+    np.testing.assert_array_equal(_quantised_query(q, 2), q)
+    assert np.abs(_quantised_query(q, 1) - q).max() > 0
+
+
+@pytest.mark.parametrize("variant", [None, "planted"])
+def test_two_e4m3_terms_of_q_hold_the_tolerance_and_one_does_not(variant):
+    x = make_inputs(7, [2000, 700], 5, 16, "fp8", page_size=64, variant=variant)
+    o2, l2, o_ref, l_ref = _outputs_with_quantised_q(x, 2)
+    o1, l1, _, _ = _outputs_with_quantised_q(x, 1)
+    max2, rel2 = _errors(o2, o_ref)
+    lse2 = np.abs(l2 - l_ref).max()
+    assert max2 <= TOL_O_MAX / 100 and rel2 <= TOL_O_REL / 100 and lse2 <= TOL_LSE / 100
+    if variant == "planted":
+        # The planted keys give a few scores of tens of units; an error of
+        # 2^-5 relative in q moves them, and the LSE with them, by more than
+        # the bound.
+        assert np.abs(l1 - l_ref).max() > TOL_LSE
