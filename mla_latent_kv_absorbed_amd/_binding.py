@@ -134,8 +134,10 @@ class Plan:
             np.int32).reshape(-1, 2)
 
     def split_reqs(self) -> np.ndarray:
+        """int32 [num_split_reqs, 4]: b, first_part, num_parts, pad."""
         h = self.header
-        return self.host[h["off_split"]:h["off_split"] + 4 * h["num_split_reqs"]].view(np.int32)
+        return self.host[h["off_split"]:h["off_split"] + 16 * h["num_split_reqs"]].view(
+            np.int32).reshape(-1, 4)
 
     def to_device(self, device="cuda"):
         import torch

@@ -6,6 +6,8 @@
 
 namespace mla {
 
+struct SplitReq;  // plan_layout.h
+
 // Element type of the KV pool (the values of mla_kv_dtype).
 enum KvKind : int { kKvBf16 = 0, kKvFp8 = 1, kKvFp4 = 2, kKvMx = 3 };
 
@@ -30,8 +32,9 @@ struct DecodeArgs {
 
 hipError_t launch_decode(int kv, bool paged, int grid, const DecodeArgs& args,
                          hipStream_t stream);
-// max_parts: the largest part count of any split request in the plan.
-hipError_t launch_merge_split(const uint8_t* plan_dev, int num_split_reqs, int rows,
+// split_dev: the plan's split-request records in device memory; max_parts:
+// the largest part count among them.
+hipError_t launch_merge_split(const SplitReq* split_dev, int num_split_reqs, int rows,
                               int max_parts, const uint16_t* ws_o, const float* ws_lse,
                               const float* ws_sc, float* out, float* lse, hipStream_t stream);
 // Device address of the current device's no-alloc scratch array (capacity

@@ -92,7 +92,7 @@ Layout layout_for(int64_t num_wgs, int64_t num_units, int64_t batch, int64_t num
   l.off_units = align_up(l.off_wg + 4 * (num_wgs + 1), 16);
   l.off_reqs = align_up(l.off_units + (int64_t)sizeof(Unit) * num_units, 16);
   l.off_split = align_up(l.off_reqs + (int64_t)sizeof(ReqParts) * batch, 16);
-  l.total = align_up(l.off_split + 4 * num_split, 16);
+  l.total = align_up(l.off_split + (int64_t)sizeof(SplitReq) * num_split, 16);
   return l;
 }
 
@@ -391,7 +391,9 @@ mla_status mla_decode_plan(const mla_decode_desc* d, const int32_t* seq_lens_hos
   }
   wgb[num_wgs] = (int32_t)k;
   std::memcpy(base + lay.off_reqs, reqs.data(), sizeof(ReqParts) * B);
-  if (!split.empty()) std::memcpy(base + lay.off_split, split.data(), 4 * split.size());
+  SplitReq* sreq = reinterpret_cast<SplitReq*>(base + lay.off_split);
+  for (size_t i = 0; i < split.size(); ++i)
+    sreq[i] = SplitReq{split[i], reqs[split[i]].first_part, reqs[split[i]].num_parts, 0};
 
   *plan_bytes = (size_t)lay.total;
   *workspace_bytes = (size_t)h->workspace_bytes;
@@ -514,13 +516,14 @@ mla_status mla_decode_merge(const void* plan_host, const void* plan_device, cons
   const float* ws_lse = reinterpret_cast<const float*>(ws + h->ws_lse_offset);
   const float* ws_sc = reinterpret_cast<const float*>(ws + h->ws_sc_offset);
   const uint8_t* blob = static_cast<const uint8_t*>(plan_host);
-  const ReqParts* reqs = reinterpret_cast<const ReqParts*>(blob + h->off_reqs);
-  const int32_t* split = reinterpret_cast<const int32_t*>(blob + h->off_split);
+  const SplitReq* split = reinterpret_cast<const SplitReq*>(blob + h->off_split);
   int max_parts = 0;
   for (int i = 0; i < h->num_split_reqs; ++i)
-    max_parts = reqs[split[i]].num_parts > max_parts ? reqs[split[i]].num_parts : max_parts;
-  if (launch_merge_split(static_cast<const uint8_t*>(plan_device), h->num_split_reqs, h->rows,
-                         max_parts, ws_o, ws_lse, ws_sc, out, lse,
+    max_parts = split[i].num_parts > max_parts ? split[i].num_parts : max_parts;
+  const SplitReq* split_dev =
+      reinterpret_cast<const SplitReq*>(static_cast<const uint8_t*>(plan_device) + h->off_split);
+  if (launch_merge_split(split_dev, h->num_split_reqs, h->rows, max_parts, ws_o, ws_lse, ws_sc,
+                         out, lse,
                          static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;

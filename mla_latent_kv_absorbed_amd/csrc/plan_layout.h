@@ -7,7 +7,7 @@
 namespace mla {
 
 constexpr uint32_t kPlanMagic = 0x504C414Du;  // "MALP"
-constexpr uint32_t kPlanVersion = 2;
+constexpr uint32_t kPlanVersion = 3;
 
 constexpr int kLatent = 512;    // kv_lora_rank: width of c_kv and of the output
 constexpr int kRope = 64;       // qk_rope_head_dim
@@ -36,7 +36,7 @@ struct PlanHeader {
   int32_t off_wg;        // int32 wg_begin[num_wgs + 1]
   int32_t off_units;     // Unit units[num_units]
   int32_t off_reqs;      // ReqParts reqs[batch]
-  int32_t off_split;     // int32 split_reqs[num_split_reqs]
+  int32_t off_split;     // SplitReq split_reqs[num_split_reqs]
   int32_t max_local;     // largest local length (table columns read)
   int32_t page_size;
   int64_t plan_bytes;
@@ -63,6 +63,16 @@ struct ReqParts {
   int32_t first_part;
   int32_t num_parts;  // 1: written directly by the decode kernel
 };
+
+// A request whose partials the merge combines, with its slots, so that a
+// merge wave finds everything it needs in one 16-byte load.
+struct SplitReq {
+  int32_t b;
+  int32_t first_part;
+  int32_t num_parts;
+  int32_t pad;
+};
+static_assert(sizeof(SplitReq) == 16, "split request layout");
 
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 

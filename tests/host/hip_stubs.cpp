@@ -85,11 +85,20 @@ hipError_t launch_decode(int kv, bool paged, int grid, const DecodeArgs& a, hipS
   return hipSuccess;
 }
 
-hipError_t launch_merge_split(const uint8_t*, int num_split_reqs, int rows, int max_parts,
+hipError_t launch_merge_split(const SplitReq* split, int num_split_reqs, int rows, int max_parts,
                               const uint16_t*, const float*, const float*, float*, float*,
                               hipStream_t) {
   ++g_merge_launches;
   REQUIRE(num_split_reqs > 0 && rows > 0 && max_parts > 1);
+  // The driver passes the host plan as the device plan, so the records can
+  // be read here: every one is split, and max_parts is their largest count.
+  int largest = 0;
+  for (int i = 0; i < num_split_reqs; ++i) {
+    REQUIRE(split[i].b >= 0 && split[i].first_part >= 0 && split[i].pad == 0);
+    REQUIRE(split[i].num_parts > 1 && split[i].num_parts <= max_parts);
+    largest = split[i].num_parts > largest ? split[i].num_parts : largest;
+  }
+  REQUIRE(largest == max_parts);
   return hipSuccess;
 }
 

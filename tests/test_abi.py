@@ -163,7 +163,7 @@ def test_decode_and_combine_reject_bad_arguments_on_host():
 def test_plan_header_fields():
     p = mla.make_plan(_desc(batch=3, dcp_size=8, dcp_rank=5), [100000, 8, 6])
     h = p.header
-    assert h["magic"] == 0x504C414D and h["version"] == 2
+    assert h["magic"] == 0x504C414D and h["version"] == 3
     assert h["rows"] == 480 and h["row_groups"] == 4
     assert h["max_local"] == 12500 and h["dcp_size"] == 8 and h["dcp_rank"] == 5
     assert h["plan_bytes"] == len(p.host) and h["page_size"] == 64

@@ -23,7 +23,11 @@ def check_plan(plan, seq_lens, q_len, H, W=1, r=0):
     assert wgb[0] == 0 and wgb[-1] == h["num_units"] and np.all(np.diff(wgb) >= 0)
     assert len(u) == h["num_units"]
     rp = plan.req_parts()
-    split = set(plan.split_reqs().tolist())
+    sr = plan.split_reqs()
+    split = set(sr[:, 0].tolist())
+    assert len(split) == len(sr) and np.all(sr[:, 3] == 0)
+    for b, first, nparts in sr[:, :3].tolist():   # each record repeats its request's slots
+        assert first == rp[b, 0] and nparts == rp[b, 1]
     seen_parts = set()
     for b in range(len(seq_lens)):
         ub = u[u[:, 0] == b]
