@@ -27,6 +27,11 @@ Statements (T = BF16 or FP8):
   MLA_STEP_FP8_ASM   QK of tile t+1, SM of tile t and PV of tile t-1, plus DMA
   MLA_SMPV_FP8_ASM   SM of tile t and PV of tile t-1 (last step)
   MLA_SM_FP8_ASM     SM alone (one-tile units)
+  MLA_LOOP_FP8_ASM   the whole tile loop of a paged FP8 unit of two or more
+                     tiles (a wave with rows): the steps above unrolled by
+                     the 8-buffer ring, each with its workgroup barrier, the
+                     DMA of tile t+6 and the table walk (fp8_loop)
+  MLA_RESCALE_ASM    O *= alpha over all 256 accumulators
 
 QK and PV MFMAs alternate one for one, so the dependent S chain never stalls
 the matrix pipe while PV MFMAs remain, and the VALU and LDS work (widening,
@@ -81,8 +86,10 @@ SM, per lane (16 scores x_i of one query row; token of x_i is
 other half of the row sits in lane ^ 32); if (m_t - mref) c2 > 8 the running
 max moves to m_t and alpha = 2^((mref - m_t) c2), else alpha = 1; lsum *= alpha;
 e_i = 2^(x_i c2 - m c2) (with m c2 floored at -FLT_MAX, so a row with nothing
-visible yet gives e = 0); lsum += sum e_i; P_i = e_i (FP8: e_i * scale_i),
-packed to BF16 with round-to-nearest-even.
+visible yet gives e = 0); lsum += sum e_i; P_i = e_i, packed to BF16 with
+round-to-nearest-even (FP8: P_i = e_i * scale_i as two e4m3 terms, hi and the
+rounded remainder lo, in units of 2^(E-8) where 2^E bounds the row's P in the
+tile; the E8M0 code of 2^(E-8) goes to %[psco] for the P.V MFMAs).
 
 DMA.  Row instruction k (k = 0..3 FP8, 0..8 BF16) moves 16 bytes per lane from
 the lane's row address + 128 k to LDS %[m0b] + 4096 k + 16 lane (the
